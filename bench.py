@@ -1,0 +1,293 @@
+"""Benchmark: one Orthrus decode round (draft pass + verify pass + consensus/commit) per step
+on a random-init Qwen3-8B-width decoder truncated to 8 layers, batch 8, 4096-token prompts,
+bf16, greedy -- synthetic seeded inputs, one MI355X.
+
+Prints ONE JSON line: accepted (committed) tokens/s over the timed rounds, round latency,
+the roofline record of the round's dominant kernel (timed live with HIP events on the
+stream it runs on), the attention roofline at the batched paged Qwen3-8B attention workload,
+the AR-step yardstick, and the CPU oracle's throughput on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--batch", type=int, default=8)
+    p.add_argument("--prompt", type=int, default=4096)
+    p.add_argument("--layers", type=int, default=8)
+    p.add_argument("--precision", default="bf16", choices=["bf16", "fp32"])
+    p.add_argument("--kv-chunk", type=int, default=1024)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-attn", action="store_true")
+    return p.parse_args()
+
+
+def event_time_ms(fn, iters=10):
+    import torch
+    fn()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(iters):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / iters
+
+
+def kernel_table(dec, ctx_np):
+    """Per-launch HIP-event times of each kernel class of the round at its in-round shapes."""
+    import orthrus_round_amd._lib as L
+    s, B, K = dec.shape, dec.B, dec.K
+    M = B * K
+    H, D, Hq, Hkv, I, V = s.hidden, s.head_dim, s.q_heads, s.kv_heads, s.inter, s.vocab
+    dt = dec.dt
+    esz = 2 if dt == L.BF16 else 4
+    Wl = dec.layers[0]
+    desc = dec._attn_desc(B, K)
+    ws = dec._ws(desc)
+    n_sum = int(ctx_np.sum())
+    tab = {}
+
+    def add(name, fn, per_round, bytes_, flops):
+        ms = event_time_ms(fn)
+        tab[name] = dict(ms=ms, per_round=per_round, bytes=bytes_, flops=flops)
+
+    add("gemm_qkv", lambda: L.gemm(M, dec.nqkv, H, dt, dt, L.EPI_STORE, dec.a, Wl["qkv_ar"], None, dec.qkv),
+        2 * s.layers, (dec.nqkv * H + M * H + M * dec.nqkv) * esz, 2 * M * dec.nqkv * H)
+    add("gemm_o_residual", lambda: L.gemm(M, H, Hq * D, dt, dt, L.EPI_RESIDUAL, dec.o, Wl["o_ar"], dec.x, dec.x),
+        2 * s.layers, (H * Hq * D + M * Hq * D + 2 * M * H) * esz, 2 * M * H * Hq * D)
+    add("gemm_gate_up_swiglu", lambda: L.gemm(M, 2 * I, H, dt, dt, L.EPI_SWIGLU, dec.a, Wl["gate_up"], None, dec.h),
+        2 * s.layers, (2 * I * H + M * H + M * I) * esz, 2 * M * 2 * I * H)
+    add("gemm_down_residual", lambda: L.gemm(M, H, I, dt, dt, L.EPI_RESIDUAL, dec.h, Wl["down"], dec.x, dec.x),
+        2 * s.layers, (H * I + M * I + 2 * M * H) * esz, 2 * M * H * I)
+    kv_b = Hkv * D * 2 * esz  # K and V bytes per key
+    qo_b = 2 * M * Hq * D * esz
+    add("attn_draft", lambda: L.draft_attn(desc, dec.q, dec.k_pages[0], dec.v_pages[0], dec.page_table, dec.ctx_len,
+                                           dec.k_blk, dec.v_blk, dec.o, ws),
+        s.layers, n_sum * kv_b + M * kv_b + qo_b, 4 * Hq * D * K * (n_sum + B * K))
+    add("attn_verify", lambda: L.verify_attn(desc, dec.q, dec.k_pages[0], dec.v_pages[0], dec.page_table,
+                                             dec.ctx_len, dec.o, ws),
+        s.layers, (n_sum + M) * kv_b + qo_b, 4 * Hq * D * K * (n_sum + B * K))
+    d = L.lmhead_desc(M, H, V, dt, K)
+    add("lmhead_argmax", lambda: L.lmhead_argmax(d, dec.a, dec.lm_head, dec.seq_id, dec.round, dec.target.view(-1),
+                                                 None, None, dec.lm_ws),
+        2, (V * H + M * H) * esz, 2 * M * V * H)
+    add("rmsnorm", lambda: L.rmsnorm(M, H, dt, dec.x, Wl["attn_norm"], s.eps, dec.a), 4 * s.layers + 2,
+        2 * M * H * esz, 0)
+    add("rope_kv_write", lambda: L.rope_kv_write(B, K, Hq, Hkv, D, dec.page, dec.max_pages, dt, dec.qkv, dec.rope,
+                                                 dec.max_pos, dec.ctx_len, None, dec.q, dec.k_blk, dec.v_blk),
+        2 * s.layers, (M * dec.nqkv + M * (Hq + 2 * Hkv) * D) * esz, 0)
+    return tab
+
+
+def roofline_of(name, rec, bound="hbm"):
+    if bound == "hbm":
+        ach = rec["bytes"] / (rec["ms"] * 1e-3) / 1e9
+        return {"kernel": name, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_launch": rec["bytes"],
+                "ms_per_launch": round(rec["ms"], 5)}
+    ach = rec["flops"] / (rec["ms"] * 1e-3) / 1e12
+    return {"kernel": name, "bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None, "flops_per_launch": rec["flops"],
+            "ms_per_launch": round(rec["ms"], 5)}
+
+
+def attention_roofline(kv_chunk):
+    """Draft + verify attention at batch 16, 32Q/8KV heads, D 128, ragged contexts 512..16384,
+    16-token pages in a seeded random order (bf16 in, fp32 out); cold L2/MALL per launch."""
+    import torch
+    import orthrus_round_amd as ora
+    import synth
+    ctx = synth.ragged_lengths(3, 16, 512, 16384)
+    inp = synth.attn_inputs(3, ctx, 32, 8, 128)
+    dv = lambda x, bf=True: (torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16) if bf
+                             else torch.from_numpy(np.ascontiguousarray(x))).cuda()
+    maxp = inp.page_table.shape[1]
+    desc = ora.attn_desc(16, 32, 8, 128, 32, 16, maxp, maxp * 16, kv_chunk, ora.BF16, ora.F32, 1.0)
+    ws = torch.empty(max(16, ora.attn_workspace_bytes(desc)), dtype=torch.uint8, device="cuda")
+    q, pk, pv = dv(inp.q), dv(np.nan_to_num(inp.pages_k)), dv(np.nan_to_num(inp.pages_v))
+    pt, cl = dv(inp.page_table, False), dv(inp.ctx, False)
+    kb, vb = dv(inp.k_blk), dv(inp.v_blk)
+    out = torch.empty((16, 32, 32, 128), dtype=torch.float32, device="cuda")
+    flush = torch.empty(512 * 2**20, dtype=torch.uint8, device="cuda")
+    res = {}
+    n_sum = int(ctx.sum())
+    for name, fn, keys in [
+        ("draft", lambda: ora.draft_attn(desc, q, pk, pv, pt, cl, kb, vb, out, ws), n_sum + 16 * 32),
+        ("verify", lambda: ora.verify_attn(desc, q, pk, pv, pt, cl, out, ws), n_sum + 16 * 32),
+    ]:
+        byts = keys * 8 * 128 * 2 * 2 + q.numel() * 2 + out.numel() * 4
+        fn()
+        times = []
+        for _ in range(20):
+            flush.fill_(1)  # evict L2 and MALL (512 MiB > 256 MiB infinity cache)
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            fn()
+            e.record()
+            torch.cuda.synchronize()
+            times.append(s.elapsed_time(e))
+        ms = float(np.median(times))
+        res[name] = {"ms": round(ms, 5), "bytes": byts, "GBs": round(byts / ms / 1e6, 1),
+                     "frac": round(byts / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    return {"workload": "batch 16, 32Q/8KV, D128, ctx U[512,16384], 16-token paged random order, bf16->fp32, cold",
+            "sum_ctx": n_sum, **res}
+
+
+def cpu_baseline(W, shape, prompts_np, tokens_per_round_seq, kv_seed=9):
+    """The CPU oracle (float64, batched BLAS rows) on a bounded sample: one draft + verify
+    round of ONE sequence through layer 0 of the 8 (plus the LM head), over a synthetic
+    4095-token AR cache; scaled to the whole model as layers x (layer time) + LM head."""
+    import dataclasses
+    from oracle import decode as Dc
+    from oracle import model as M
+    import synth
+    one = dataclasses.replace(shape, layers=1)
+    keys = ["embed", "lm_head", "final_norm"] + [k for k in W if k.startswith("0.")]
+    Wt = M.Weights({k: W[k] for k in keys}, one)
+    P = prompts_np.shape[1]
+    cache = Dc.Cache(one, P + 64, np.float64)
+    rs = np.random.default_rng(kv_seed)
+    cache.k[0][: P - 1] = rs.standard_normal((P - 1, one.kv_heads, one.head_dim))
+    cache.v[0][: P - 1] = rs.standard_normal((P - 1, one.kv_heads, one.head_dim))
+    cache.n = P - 1
+    anchor = int(prompts_np[0, -1])
+    nthreads = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    zd = Dc.draft_pass(Wt, cache, [anchor] + [one.mask_id] * 31, rowwise=False)
+    t1 = time.perf_counter()
+    zt = Dc.ar_pass(Wt, cache, [anchor] + list(M.argmax_lowest(zd)[:31]), rowwise=False)
+    t2 = time.perf_counter()
+    # LM head share: time it alone to separate it from the layer
+    h = np.ones((32, one.hidden))
+    t3 = time.perf_counter()
+    M.lm_logits(Wt, h, rowwise=False)
+    t4 = time.perf_counter()
+    lm = t4 - t3
+    layer = (t2 - t0) - 2 * lm
+    full_round = shape.layers * layer + 2 * lm
+    value = tokens_per_round_seq / full_round
+    return {"value": round(value, 4), "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": (f"float64 NumPy oracle, one round (draft+verify) of 1 sequence through layer 0 plus the LM "
+                       f"head over a synthetic {P - 1}-token cache; measured {t2 - t0:.2f}s, scaled to "
+                       f"{shape.layers} layers = {full_round:.2f}s per round at the GPU's "
+                       f"{tokens_per_round_seq:.3f} committed tokens per round per sequence"),
+            "round_s": round(full_round, 3)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode round is sharded by "
+              "sequence across GPUs with no exchange, so N GPUs = N independent copies of this run.")
+        sys.exit(2)
+    import torch
+    import synth
+    from orthrus_round_amd.decoder import Decoder
+    import orthrus_round_amd as ora
+    ora.lib()
+    t_setup = time.perf_counter()
+    shape = synth.QWEN3_8B_L8
+    if args.layers != shape.layers:
+        import dataclasses
+        shape = dataclasses.replace(shape, layers=args.layers)
+    W = synth.model_weights(shape, cfg=5, diff_std=0.002, bf16=True)
+    prompts = synth.prompt_ids(shape, 5, args.batch, args.prompt)
+    total_rounds = args.warmup + args.steps + 2
+    dec = Decoder(W, shape, precision=args.precision, block=32, max_batch=args.batch,
+                  max_ctx=args.prompt + 32 * total_rounds + 64, kv_chunk=args.kv_chunk)
+    print(f"[bench] setup {time.perf_counter() - t_setup:.1f}s", file=sys.stderr, flush=True)
+    dec.prefill(torch.from_numpy(prompts), max_out=32 * total_rounds)
+    torch.cuda.synchronize()
+    g = dec.capture(dec.round_greedy)  # its warm-up call is one untimed round
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    out0 = int(dec.out_len.sum())
+    r0 = dec.round.cpu().numpy().copy()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        g.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    committed = int(dec.out_len.sum()) - out0
+    elapsed = t1 - t0
+    rounds_done = int((dec.round.cpu().numpy() - r0).min())
+    ctx_np = dec.ctx_len.cpu().numpy()
+    print(f"[bench] {args.steps} rounds in {elapsed:.3f}s, committed {committed}", file=sys.stderr, flush=True)
+
+    tab = kernel_table(dec, ctx_np)
+    per_round = {k: v["ms"] * v["per_round"] for k, v in tab.items()}
+    dominant = max(per_round, key=per_round.get)
+    roof = roofline_of(dominant, tab[dominant], "mfma" if dominant == "lmhead_argmax" and args.batch * 32 >= 512
+                       else "hbm")
+
+    # AR yardstick on the same kernels (one causal row per sequence per step)
+    dec.prefill(torch.from_numpy(prompts), max_out=64)
+    ga = dec.capture(dec.ar_step)
+    for _ in range(3):
+        ga.replay()
+    torch.cuda.synchronize()
+    ta = time.perf_counter()
+    for _ in range(20):
+        ga.replay()
+    torch.cuda.synchronize()
+    ar_ms = (time.perf_counter() - ta) / 20 * 1e3
+
+    attn = None if args.no_attn else attention_roofline(args.kv_chunk)
+    tokens_per_round_seq = committed / (args.steps * args.batch)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(W, shape, prompts, tokens_per_round_seq)
+
+    ms = elapsed / args.steps * 1e3
+    rec = {
+        "metric": "accepted tokens/s (Orthrus decode rounds, committed tokens)",
+        "value": round(committed / elapsed, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": args.precision,
+        "data": "synthetic (seeded random-init weights N(0,0.02), diffusion view = AR + N(0,0.002), uniform prompt ids)",
+        "config": {"workload": "Orthrus round, Qwen3-8B width truncated to %d layers, greedy" % shape.layers,
+                   "batch": args.batch, "prompt_len": args.prompt, "block": 32, "hidden": shape.hidden,
+                   "heads": f"{shape.q_heads}Q/{shape.kv_heads}KV x {shape.head_dim}", "inter": shape.inter,
+                   "vocab": shape.vocab, "kv_chunk": args.kv_chunk, "parallelism": "single GPU"},
+        "round_latency_ms": round(ms, 4),
+        "tokens_per_round_per_seq": round(tokens_per_round_seq, 4),
+        "tpf": round(tokens_per_round_seq / 2, 4),
+        "rounds_timed_min": rounds_done,
+        "ar_step_ms": round(ar_ms, 4),
+        "ar_tokens_per_s": round(args.batch / ar_ms * 1e3, 2),
+        "projected_tokens_per_s_at_pages_10p78_tokens_per_round": round(args.batch * 10.78 / ms * 1e3, 1),
+        "roofline": roof,
+        "kernels": {k: {"ms": round(v["ms"], 5), "per_round": v["per_round"],
+                        "GBs": round(v["bytes"] / v["ms"] / 1e6, 1)} for k, v in tab.items()},
+        "attention_roofline": attn,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

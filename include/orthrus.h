@@ -1,0 +1,234 @@
+/*
+ * orthrus.h -- C ABI of the Orthrus decode-round kernels for AMD Instinct MI355X (gfx950).
+ *
+ * One Orthrus round (Orthrus paper summary, cjcn.com.cn, sec. 四 "inference"):
+ *   (1) the diffusion view drafts a block of K = 32 tokens in one parallel pass from the
+ *       anchor plus [MASK] placeholders, attending to the shared AR cache before the anchor
+ *       and bidirectionally to its own block      -> orthrus_draft_attn, orthrus_lmhead_argmax
+ *   (2) the frozen AR path verifies all K positions in one causal pass
+ *                                                  -> orthrus_verify_attn, orthrus_lmhead_argmax
+ *   (3) intra-model consensus: accept the longest left-to-right prefix where draft == AR
+ *       choice, emit the AR token at the first mismatch, discard the rest, update the cache
+ *                                                  -> orthrus_consensus_commit
+ *       (temperature > 0: strict rejection sampling) -> orthrus_rejection_accept
+ * The support calls (GEMM with fused epilogues, RMSNorm, RoPE + K/V write, block embedding)
+ * run the decoder layers of both views so that every step of the round is a kernel here.
+ *
+ * Conventions shared by every call
+ *  - All tensor arguments are DEVICE pointers owned by the caller; the library never
+ *    allocates, frees or synchronises.  Scratch memory is a caller-provided workspace sized
+ *    by the matching *_workspace_bytes query.
+ *  - `stream` is a hipStream_t passed as void*; every call only enqueues work on it.
+ *  - Row-major layouts; element type given by an orthrus_dtype_t (bf16 or fp32).
+ *  - Arguments are validated on the host before anything is enqueued.  A non-zero
+ *    orthrus_status_t means nothing was launched; orthrus_last_error() (thread-local) says why.
+ *    ORTHRUS_ERR_HIP means a launch failed; asynchronous device faults surface at the
+ *    caller's next synchronisation, as usual for HIP.
+ *  - Round state (ctx_len, anchor, out_len, round, done) lives in device memory and is
+ *    updated in place by the commit calls, so a round needs no host round-trip.
+ *  - No call keeps mutable global state apart from the thread-local error string.
+ */
+#ifndef ORTHRUS_H_
+#define ORTHRUS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ORTHRUS_ABI_VERSION 1
+
+typedef enum {
+  ORTHRUS_OK = 0,
+  ORTHRUS_ERR_INVALID_ARG = 1, /* null pointer, bad size, inconsistent shape          */
+  ORTHRUS_ERR_UNSUPPORTED = 2, /* valid but not implemented (head_dim, group, dtype)    */
+  ORTHRUS_ERR_WORKSPACE = 3,   /* workspace smaller than the *_workspace_bytes query    */
+  ORTHRUS_ERR_HIP = 4          /* a HIP launch returned an error                        */
+} orthrus_status_t;
+
+typedef enum { ORTHRUS_BF16 = 0, ORTHRUS_F32 = 1 } orthrus_dtype_t;
+
+/* Philox4x64-10 stream ids (second key word); the first key word is the caller's seed. */
+enum { ORTHRUS_STREAM_DRAFT = 1, ORTHRUS_STREAM_ACCEPT = 2, ORTHRUS_STREAM_RESID = 3, ORTHRUS_STREAM_AR = 4 };
+
+int32_t orthrus_abi_version(void);
+const char* orthrus_last_error(void);
+
+/* ------------------------------------------------------------------------------------------
+ * Dual-view block attention (Orthrus paper summary, sec. 二: the diffusion query attends to
+ * concat(K_AR, K_diff) / concat(V_AR, V_diff); sec. 三: draft mask = AR context before the
+ * anchor + the whole own block, AR path = causal mask).
+ *
+ * Shapes (G = q_heads / kv_heads; query head h reads kv head h / G):
+ *   q          [batch, block, q_heads, head_dim]          dtype
+ *   k_pages,
+ *   v_pages    [num_pages, kv_heads, page_size, head_dim]  dtype   (paged AR cache)
+ *   page_table [batch, max_pages] int32: logical page p of sequence b -> physical page
+ *   ctx_len    [batch] int32: n_b = number of cached keys before the block (= anchor position)
+ *   k_blk,
+ *   v_blk      [batch, block, kv_heads, head_dim]          dtype   (draft: the block's own keys)
+ *   out        [batch, block, q_heads, head_dim]           out_dtype
+ * Keys are visited in fixed 32-key tiles at absolute positions and split into fixed chunks
+ * of kv_chunk keys that are combined in chunk order, so a query row's result does not depend
+ * on block size, batch composition or page order (same inputs -> same bits).
+ * Device-side: a sequence with n_b + block > max_ctx writes NaN rows (host cannot see n_b).
+ * ------------------------------------------------------------------------------------------ */
+typedef struct {
+  int32_t batch;
+  int32_t q_heads;
+  int32_t kv_heads;   /* q_heads % kv_heads == 0, group in {1, 2, 4, 8}            */
+  int32_t head_dim;   /* 64 or 128                                                  */
+  int32_t block;      /* rows per sequence, 1..32                                   */
+  int32_t page_size;  /* keys per page, a divisor of 32 or a multiple of 32         */
+  int32_t max_pages;  /* row length of page_table                                   */
+  int32_t max_ctx;    /* bound on n_b + block; <= max_pages * page_size             */
+  int32_t kv_chunk;   /* keys per split chunk, multiple of 32 (0 = 1024)            */
+  int32_t dtype;      /* orthrus_dtype_t of q, pages and block keys/values          */
+  int32_t out_dtype;  /* orthrus_dtype_t of out                                     */
+  float scale;        /* softmax scale applied to q.k                               */
+} orthrus_attn_desc_t;
+
+size_t orthrus_attn_workspace_bytes(const orthrus_attn_desc_t* desc);
+
+/* Draft (diffusion-view) attention: slot i of sequence b attends to cache keys [0, n_b) and to
+ * all `block` keys of k_blk/v_blk[b] (bidirectional inside the block). */
+int32_t orthrus_draft_attn(const orthrus_attn_desc_t* desc, const void* q, const void* k_pages,
+                           const void* v_pages, const int32_t* page_table, const int32_t* ctx_len,
+                           const void* k_blk, const void* v_blk, void* out, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Verify (AR-view) attention: the block's own keys are already in the cache at
+ * [n_b, n_b + block); slot j attends to cache keys [0, n_b + j] (causal). */
+int32_t orthrus_verify_attn(const orthrus_attn_desc_t* desc, const void* q, const void* k_pages,
+                            const void* v_pages, const int32_t* page_table, const int32_t* ctx_len,
+                            void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * LM head with fused token choice (sec. 四 steps 1-2: each pass yields one token per slot).
+ *   h [rows, hidden], w [vocab, hidden] (dtype); z = h w^T accumulated in fp32.
+ *   temperature == 0: token_out[r] = argmax_x z[r, x], exact ties -> lowest id.
+ *   temperature  > 0: token_out[r] = argmax_x (z[r,x]/T - ln(-ln u[r,x])) (Gumbel-max, a sample
+ *     of softmax(z/T)); u from Philox4x64-10 with key (seed, stream_id) and, for row
+ *     r = b*block + s, counter (s/4, x, round[b], seq_id[b]) and output word s%4; the
+ *     uniform is ((word >> 41) + 0.5) * 2^-23.
+ *   logits_out [rows, vocab] fp32 (optional, may be NULL): z.
+ *   lse_out [rows] fp32 (optional): logsumexp_x(z[r,x] / T) (T = 1 when temperature == 0).
+ *   seq_id, round [rows / block] int32: required when temperature > 0, else may be NULL.
+ * Supported: dtype bf16 or fp32; hidden % 64 == 0.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct {
+  int32_t rows;
+  int32_t hidden;
+  int32_t vocab;
+  int32_t dtype;
+  int32_t block;       /* rows per sequence (RNG counters); rows % block == 0 */
+  int32_t stream_id;   /* ORTHRUS_STREAM_DRAFT or ORTHRUS_STREAM_AR             */
+  float temperature;
+  uint64_t seed;
+} orthrus_lmhead_desc_t;
+
+size_t orthrus_lmhead_workspace_bytes(const orthrus_lmhead_desc_t* desc);
+int32_t orthrus_lmhead_argmax(const orthrus_lmhead_desc_t* desc, const void* h, const void* w,
+                              const int32_t* seq_id, const int32_t* round, int32_t* token_out,
+                              float* logits_out, float* lse_out, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Greedy consensus + commit (sec. 四 step 3), one wavefront per sequence, no host round-trip.
+ *   draft [batch, block]  = d_1..d_K (diffusion view's choice for positions n+1..n+K)
+ *   target [batch, block] = t_1..t_K (AR choice at the same positions)
+ * For each sequence b with done[b] == 0:
+ *   k = number of leading i with d_i == t_i (0..K); emitted = d_1..d_k, then t_{k+1} if k < K;
+ *   the emitted tokens are appended to out_tokens[b, out_len[b] ...] (truncated at max_out);
+ *   anchor[b] = last emitted token; ctx_len[b] += min(k + 1, K) (the rollback: cache slots at
+ *   and beyond the new ctx_len are dead and get overwritten by the next verify);
+ *   accept[b] = k; round[b] += 1; done[b] = 1 once out_len[b] >= max_out, or -1 if the next
+ *   round would not fit (ctx_len[b] + K > max_ctx).  Sequences with done[b] != 0 are untouched
+ *   except accept[b] = -1.
+ * ------------------------------------------------------------------------------------------ */
+int32_t orthrus_consensus_commit(int32_t batch, int32_t block, const int32_t* draft,
+                                 const int32_t* target, int32_t* ctx_len, int32_t* anchor,
+                                 int32_t* accept, int32_t* out_tokens, int32_t* out_len,
+                                 int32_t* round, int32_t* done, int32_t max_out, int32_t max_ctx,
+                                 void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Rejection-sampling accept + commit at temperature > 0 (sec. 四: strict rejection sampling
+ * keeps the AR distribution; rule of standard speculative sampling).
+ *   draft_logits, target_logits [batch, block, vocab] fp32 (z, before the temperature)
+ *   draft_lse, target_lse [batch, block] fp32: logsumexp(z / T) as written by the LM head
+ *   draft [batch, block]: the sampled drafts d_1..d_K
+ * Slot i (in order) accepts d_i iff u_i * q_i(d_i) < p_i(d_i), q = softmax(z_draft/T),
+ * p = softmax(z_target/T), u_i from Philox (key (seed, ACCEPT), counter (i/4, 0, round[b],
+ * seq_id[b]), word i%4).  At the first rejection j the token is drawn from max(0, p_j - q_j)
+ * (from p_j if that has no mass) by exponential race argmax_x r(x) / E_x, E_x = -ln u_x with
+ * u_x from (seed, RESID), counter (x/4, 0, round[b], seq_id[b]), word x%4; ties -> lowest id.
+ * Then the same commit as orthrus_consensus_commit.
+ * ------------------------------------------------------------------------------------------ */
+size_t orthrus_rejection_workspace_bytes(int32_t batch);
+int32_t orthrus_rejection_accept(int32_t batch, int32_t block, int32_t vocab, float temperature,
+                                 uint64_t seed, const int32_t* seq_id, const float* draft_logits,
+                                 const float* target_logits, const float* draft_lse,
+                                 const float* target_lse, const int32_t* draft, int32_t* ctx_len,
+                                 int32_t* anchor, int32_t* accept, int32_t* out_tokens,
+                                 int32_t* out_len, int32_t* round, int32_t* done, int32_t max_out,
+                                 int32_t max_ctx, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Support kernels for the decoder layers of both views.
+ * ------------------------------------------------------------------------------------------ */
+typedef enum {
+  ORTHRUS_EPI_STORE = 0,    /* c = a w^T                                                     */
+  ORTHRUS_EPI_RESIDUAL = 1, /* c = residual + a w^T (c may alias residual)                   */
+  ORTHRUS_EPI_SWIGLU = 2    /* w holds gate/up rows interleaved in 32-row groups
+                               (see orthrus_pack_gate_up); c[m, j] = silu(g) * u, N/2 columns */
+} orthrus_epilogue_t;
+
+/* c [M, N'] = epilogue(a [M, K] . w [N, K]^T), fp32 accumulation in a fixed k order (the
+ * result of an output element never depends on M).  K % 64 == 0, N % 64 == 0. */
+int32_t orthrus_gemm(int32_t M, int32_t N, int32_t K, int32_t dtype, int32_t out_dtype,
+                     int32_t epilogue, const void* a, const void* w, const void* residual, void* c,
+                     void* stream);
+
+/* Interleave gate [I, H] and up [I, H] into [2I, H] in 32-row groups: gate 0..31, up 0..31,
+ * gate 32..63, ... (I % 32 == 0). */
+int32_t orthrus_pack_gate_up(int32_t inter, int32_t hidden, int32_t dtype, const void* gate,
+                             const void* up, void* packed, void* stream);
+
+/* y [rows, hidden] = x / sqrt(mean(x^2) + eps) * gain, fp32 math; x and y in `dtype`. */
+int32_t orthrus_rmsnorm(int32_t rows, int32_t hidden, int32_t dtype, const void* x,
+                        const float* gain, float eps, void* y, void* stream);
+
+/* table [max_pos, head_dim/2, 2] fp32 = (cos, sin) of pos * base^(-2i/D), evaluated in fp64. */
+int32_t orthrus_rope_table(int32_t max_pos, int32_t head_dim, double base, float* table,
+                           void* stream);
+
+/* Split a QKV projection [batch*block, (Hq + 2 Hkv) * D] (q | k | v), apply rotate-half RoPE at
+ * positions ctx_len[b] + s to q and k, write q_out [batch*block, Hq*D] and K/V either into the
+ * paged cache at positions [ctx_len[b], ctx_len[b] + block) (page_table != NULL) or into
+ * k_blk/v_blk [batch, block, Hkv, D] (page_table == NULL). */
+int32_t orthrus_rope_kv_write(int32_t batch, int32_t block, int32_t q_heads, int32_t kv_heads,
+                              int32_t head_dim, int32_t page_size, int32_t max_pages, int32_t dtype,
+                              const void* qkv, const float* rope_table, int32_t max_pos,
+                              const int32_t* ctx_len, const int32_t* page_table, void* q_out,
+                              void* k_dst, void* v_dst, void* stream);
+
+/* x [batch*block, hidden] = embed[token(b, s)] where token(b, 0) = anchor[b] if anchor != NULL;
+ * other slots read tokens[b * tok_stride + tok_offset + s - (anchor != NULL)] if tokens != NULL,
+ * else mask_id. */
+int32_t orthrus_embed_block(int32_t batch, int32_t block, int32_t hidden, int32_t dtype,
+                            const void* embed, const int32_t* anchor, const int32_t* tokens,
+                            int32_t tok_stride, int32_t tok_offset, int32_t mask_id, void* x,
+                            void* stream);
+
+/* Philox4x64-10 words for n counters (ctr [n, 4], out [n, 4] uint64), key (k0, k1). */
+int32_t orthrus_philox4x64(int64_t n, const uint64_t* ctr, uint64_t k0, uint64_t k1,
+                           uint64_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ORTHRUS_H_ */

@@ -1,0 +1,212 @@
+// Intra-model consensus and commit (greedy), the rejection-sampling accept (temperature > 0)
+// and a Philox4x64-10 word generator.
+//
+// Orthrus paper summary (cjcn.com.cn), sec. 四 step 3: compare left to right, accept while the
+// draft equals the AR choice, emit the AR choice at the first disagreement, drop the rest and
+// update the memory; at least one token per round.  With a temperature, strict rejection
+// sampling (standard speculative sampling: accept with min(1, p/q), else draw from the
+// normalised residual max(0, p - q)) keeps the AR distribution.
+//
+// The KV rollback is a length update only: slots at or beyond the new ctx_len are dead and the
+// next verify pass overwrites them.
+#include "common.hpp"
+
+namespace orthrus {
+namespace {
+
+struct CommitState {
+  int32_t* ctx_len;
+  int32_t* anchor;
+  int32_t* accept;
+  int32_t* out_tokens;
+  int32_t* out_len;
+  int32_t* round;
+  int32_t* done;
+  int32_t max_out, max_ctx;
+};
+
+// Emit `count` tokens (token i provided by lane i) for sequence b; lanes < 32 participate.
+__device__ __forceinline__ void commit_tokens(const CommitState& cs, int b, int K, int k, int count, int my_tok,
+                                              int last_tok, int lane) {
+  const int ol = cs.out_len[b];
+  if (lane < count && ol + lane < cs.max_out) cs.out_tokens[(size_t)b * cs.max_out + ol + lane] = my_tok;
+  if (lane == 0) {
+    const int written = max(0, min(count, cs.max_out - ol));
+    const int nol = ol + written;
+    const int nctx = cs.ctx_len[b] + count;
+    cs.out_len[b] = nol;
+    cs.anchor[b] = last_tok;
+    cs.ctx_len[b] = nctx;
+    cs.accept[b] = k;
+    cs.round[b] = cs.round[b] + 1;
+    cs.done[b] = nol >= cs.max_out ? 1 : (nctx + K > cs.max_ctx ? -1 : 0);
+  }
+}
+
+__global__ __launch_bounds__(64) void consensus_kernel(int K, const int32_t* __restrict__ draft,
+                                                       const int32_t* __restrict__ target, CommitState cs) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  if (cs.done[b] != 0) {
+    if (lane == 0) cs.accept[b] = -1;
+    return;
+  }
+  int d = 0, t = 0;
+  if (lane < K) {
+    d = draft[(size_t)b * K + lane];
+    t = target[(size_t)b * K + lane];
+  }
+  const uint64_t mism = __ballot(lane < K && d != t);
+  const int k = mism ? __builtin_ctzll(mism) : K;   // accepted drafts
+  const int count = min(k + 1, K);                   // tokens committed this round
+  const int tk = __shfl(t, min(k, K - 1), 64);       // correction t_{k+1}
+  const int my_tok = lane < k ? d : tk;
+  const int last_tok = __shfl(my_tok, count - 1, 64);
+  commit_tokens(cs, b, K, k, count, my_tok, last_tok, lane);
+}
+
+// One workgroup per sequence.
+__global__ __launch_bounds__(256) void rejection_kernel(int K, int V, float inv_t, uint64_t seed,
+                                                        const int32_t* __restrict__ seq_id,
+                                                        const float* __restrict__ zd, const float* __restrict__ zt,
+                                                        const float* __restrict__ lse_d,
+                                                        const float* __restrict__ lse_t,
+                                                        const int32_t* __restrict__ draft, CommitState cs) {
+  __shared__ uint64_t red[4];
+  __shared__ int s_any[4];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (cs.done[b] != 0) {
+    if (tid == 0) cs.accept[b] = -1;
+    return;
+  }
+  const int rnd = cs.round[b], sid = seq_id[b];
+  // acceptance of slot i: u_i * q_i(d_i) < p_i(d_i)
+  int k;
+  {
+    bool acc = true;
+    int d = 0;
+    if (lane < K) {
+      d = draft[(size_t)b * K + lane];
+      const size_t row = (size_t)b * K + lane;
+      const float q = expf(zd[row * V + d] * inv_t - lse_d[row]);
+      const float p = expf(zt[row * V + d] * inv_t - lse_t[row]);
+      const float u = philox_uniform(seed, ORTHRUS_STREAM_ACCEPT, lane, 0, rnd, sid);
+      acc = u * q < p;
+    }
+    const uint64_t rej = __ballot(lane < K && !acc);
+    k = rej ? __builtin_ctzll(rej) : K;
+  }
+  int corr = 0;
+  if (k < K) {
+    // residual race over the vocabulary for slot k: argmax_x r(x) / E_x, E_x = -ln u_x
+    const size_t row = (size_t)b * K + k;
+    const float ld = lse_d[row], lt = lse_t[row];
+    const float* zdr = zd + row * V;
+    const float* ztr = zt + row * V;
+    for (int pass = 0; pass < 2; ++pass) {
+      uint64_t best = 0;
+      int any = 0;
+      for (int x0 = tid * 4; x0 < V; x0 += 256 * 4) {
+        const u64x4 wd = philox4x64_10((uint64_t)(x0 >> 2), 0, (uint64_t)rnd, (uint64_t)sid, seed, ORTHRUS_STREAM_RESID);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int x = x0 + e;
+          if (x >= V) break;
+          const float p = expf(ztr[x] * inv_t - lt);
+          float rr;
+          if (pass == 0) rr = fmaxf(p - expf(zdr[x] * inv_t - ld), 0.0f);
+          else rr = p;  // residual had no mass: fall back to p
+          if (rr > 0.0f) {
+            any = 1;
+            const float E = -logf(word_to_uniform(wd.x[e]));
+            best = umax64(best, pack_argmax(rr / E, x));
+          }
+        }
+      }
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) best = umax64(best, shfl_xor_u64(best, off));
+      any = __any(any);
+      if (lane == 0) { red[w] = best; s_any[w] = any; }
+      __syncthreads();
+      best = umax64(umax64(red[0], red[1]), umax64(red[2], red[3]));
+      any = s_any[0] | s_any[1] | s_any[2] | s_any[3];
+      __syncthreads();
+      if (any || pass == 1) { corr = unpack_idx(best); break; }
+    }
+  }
+  if (w == 0) {
+    const int count = min(k + 1, K);
+    const int d = lane < K ? draft[(size_t)b * K + lane] : 0;
+    const int my_tok = lane < k ? d : corr;
+    const int last_tok = __shfl(my_tok, count - 1, 64);
+    commit_tokens(cs, b, K, k, count, my_tok, last_tok, lane);
+  }
+}
+
+__global__ void philox_kernel(int64_t n, const uint64_t* ctr, uint64_t k0, uint64_t k1, uint64_t* out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const u64x4 w = philox4x64_10(ctr[4 * i], ctr[4 * i + 1], ctr[4 * i + 2], ctr[4 * i + 3], k0, k1);
+  for (int e = 0; e < 4; ++e) out[4 * i + e] = w.x[e];
+}
+
+int32_t check_state(int batch, int block, const int32_t* ctx_len, const int32_t* anchor, const int32_t* accept,
+                    const int32_t* out_tokens, const int32_t* out_len, const int32_t* round, const int32_t* done,
+                    int max_out, int max_ctx) {
+  ORTHRUS_REQUIRE(batch >= 0 && block >= 1 && block <= 32, ORTHRUS_ERR_INVALID_ARG, "commit: batch %d / block %d",
+                  batch, block);
+  ORTHRUS_REQUIRE(max_out >= 0 && max_ctx >= block, ORTHRUS_ERR_INVALID_ARG, "commit: max_out / max_ctx");
+  ORTHRUS_REQUIRE(ctx_len && anchor && accept && out_len && round && done && (out_tokens || max_out == 0),
+                  ORTHRUS_ERR_INVALID_ARG, "commit: null state pointer");
+  return ORTHRUS_OK;
+}
+
+}  // namespace
+}  // namespace orthrus
+
+using namespace orthrus;
+
+extern "C" int32_t orthrus_consensus_commit(int32_t batch, int32_t block, const int32_t* draft, const int32_t* target,
+                                            int32_t* ctx_len, int32_t* anchor, int32_t* accept, int32_t* out_tokens,
+                                            int32_t* out_len, int32_t* round, int32_t* done, int32_t max_out,
+                                            int32_t max_ctx, void* stream) {
+  if (int32_t s = check_state(batch, block, ctx_len, anchor, accept, out_tokens, out_len, round, done, max_out, max_ctx))
+    return s;
+  ORTHRUS_REQUIRE(draft && target, ORTHRUS_ERR_INVALID_ARG, "commit: null draft/target");
+  if (batch == 0) return ORTHRUS_OK;
+  CommitState cs{ctx_len, anchor, accept, out_tokens, out_len, round, done, max_out, max_ctx};
+  hipLaunchKernelGGL(consensus_kernel, dim3(batch), dim3(64), 0, reinterpret_cast<hipStream_t>(stream), block, draft,
+                     target, cs);
+  return check_launch("orthrus_consensus_commit");
+}
+
+extern "C" size_t orthrus_rejection_workspace_bytes(int32_t batch) { (void)batch; return 0; }
+
+extern "C" int32_t orthrus_rejection_accept(int32_t batch, int32_t block, int32_t vocab, float temperature,
+                                            uint64_t seed, const int32_t* seq_id, const float* draft_logits,
+                                            const float* target_logits, const float* draft_lse,
+                                            const float* target_lse, const int32_t* draft, int32_t* ctx_len,
+                                            int32_t* anchor, int32_t* accept, int32_t* out_tokens, int32_t* out_len,
+                                            int32_t* round, int32_t* done, int32_t max_out, int32_t max_ctx,
+                                            void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace; (void)workspace_bytes;
+  if (int32_t s = check_state(batch, block, ctx_len, anchor, accept, out_tokens, out_len, round, done, max_out, max_ctx))
+    return s;
+  ORTHRUS_REQUIRE(vocab > 0 && temperature > 0.0f && std::isfinite(temperature), ORTHRUS_ERR_INVALID_ARG,
+                  "rejection: vocab > 0 and finite temperature > 0 required");
+  ORTHRUS_REQUIRE(seq_id && draft_logits && target_logits && draft_lse && target_lse && draft, ORTHRUS_ERR_INVALID_ARG,
+                  "rejection: null pointer");
+  if (batch == 0) return ORTHRUS_OK;
+  CommitState cs{ctx_len, anchor, accept, out_tokens, out_len, round, done, max_out, max_ctx};
+  hipLaunchKernelGGL(rejection_kernel, dim3(batch), dim3(256), 0, reinterpret_cast<hipStream_t>(stream), block, vocab,
+                     1.0f / temperature, seed, seq_id, draft_logits, target_logits, draft_lse, target_lse, draft, cs);
+  return check_launch("orthrus_rejection_accept");
+}
+
+extern "C" int32_t orthrus_philox4x64(int64_t n, const uint64_t* ctr, uint64_t k0, uint64_t k1, uint64_t* out,
+                                      void* stream) {
+  ORTHRUS_REQUIRE(n >= 0 && (n == 0 || (ctr && out)), ORTHRUS_ERR_INVALID_ARG, "philox: bad args");
+  if (n == 0) return ORTHRUS_OK;
+  hipLaunchKernelGGL(philox_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), n, ctr, k0, k1, out);
+  return check_launch("orthrus_philox4x64");
+}

@@ -1,0 +1,210 @@
+// LM head with fused token choice: z = h W_lm^T on MFMA, and in the same kernel the per-tile
+// argmax (greedy) or Gumbel-max sample (temperature > 0), the per-tile logsumexp partials and
+// optionally the fp32 logits.  A second small kernel merges the per-tile partials of each row
+// in tile order (deterministic: no atomics, ties -> lowest id).
+//
+// Orthrus paper summary (cjcn.com.cn), sec. 四: each pass turns the block rows into one token
+// per slot -- the diffusion view's candidates in step 1, the AR model's own choice in step 2.
+#include "gemm_core.hpp"
+
+namespace orthrus {
+namespace {
+
+struct LmArgs {
+  const void* h;
+  const void* w;
+  const int32_t* seq_id;
+  const int32_t* round;
+  float* logits;
+  uint64_t* part_best;  // [rows, ntiles]
+  float* part_m;        // [rows, ntiles] max of z/T
+  float* part_s;        // [rows, ntiles] sum exp(z/T - max)
+  int32_t M, N, K, block, ntiles;
+  float inv_t;          // 1/T (1 when greedy)
+  int32_t sample;       // temperature > 0
+  uint64_t seed, stream_id;
+};
+
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  const float M = fmaxf(m, m2);
+  s = s * expf(m - M) + s2 * expf(m2 - M);
+  m = M;
+}
+
+template <typename T, typename Cfg>
+__global__ __launch_bounds__(256) void lmhead_kernel(LmArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  T* lds = reinterpret_cast<T*>(smem);
+  const int mtiles = (a.M + Cfg::BM - 1) / Cfg::BM;
+  int mt, nt;
+  xcd_tile_map(blockIdx.x, gridDim.x, mtiles, mt, nt);
+  const int m0 = mt * Cfg::BM, n0 = nt * Cfg::BN;
+  f32x16 acc[Cfg::TM][Cfg::TN];
+  gemm_mainloop<T, Cfg>(reinterpret_cast<const T*>(a.h), reinterpret_cast<const T*>(a.w), a.M, a.N, a.K, m0, n0, lds, acc);
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hh = lane >> 5, r = lane & 31;
+  const int wm = w / Cfg::WN, wn = w % Cfg::WN;
+  __syncthreads();  // LDS is reused below
+  uint64_t* red_best = reinterpret_cast<uint64_t*>(smem);                 // [BM][WN]
+  float* red_m = reinterpret_cast<float*>(red_best + Cfg::BM * Cfg::WN);  // [BM][WN]
+  float* red_s = red_m + Cfg::BM * Cfg::WN;
+
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int mrow = (wm * Cfg::TM + i) * 32 + acc_row(e, hh);
+      const int m = m0 + mrow;
+      const bool mok = m < a.M;
+      int bseq = 0, slot = 0;
+      if (a.sample && mok) { bseq = m / a.block; slot = m % a.block; }
+      uint64_t best = 0;
+      float lm = -__builtin_huge_valf(), ls = 0.0f;
+#pragma unroll
+      for (int j = 0; j < Cfg::TN; ++j) {
+        const int n = n0 + (wn * Cfg::TN + j) * 32 + r;
+        if (!mok || n >= a.N) continue;
+        const float z = acc[i][j][e];
+        if (a.logits) a.logits[(size_t)m * a.N + n] = z;
+        const float zt = z * a.inv_t;
+        float key = z;
+        if (a.sample) {
+          const float u = philox_uniform(a.seed, a.stream_id, slot, n, a.round[bseq], a.seq_id[bseq]);
+          key = zt - logf(-logf(u));
+        }
+        best = umax64(best, pack_argmax(key, n));
+        if (zt > lm) { ls = ls * expf(lm - zt) + 1.0f; lm = zt; }
+        else ls += expf(zt - lm);
+      }
+      // reduce over the 32 columns held by this half-wave (same rows), fixed pattern
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) {
+        best = umax64(best, shfl_xor_u64(best, off));
+        const float m2 = shfl_xor_f(lm, off), s2 = shfl_xor_f(ls, off);
+        if (m2 != -__builtin_huge_valf()) {
+          if (lm == -__builtin_huge_valf()) { lm = m2; ls = s2; }
+          else lse_merge(lm, ls, m2, s2);
+        }
+      }
+      if (r == 0) {
+        red_best[mrow * Cfg::WN + wn] = best;
+        red_m[mrow * Cfg::WN + wn] = lm;
+        red_s[mrow * Cfg::WN + wn] = ls;
+      }
+    }
+  }
+  __syncthreads();
+  for (int mrow = threadIdx.x; mrow < Cfg::BM; mrow += 256) {
+    const int m = m0 + mrow;
+    if (m >= a.M) continue;
+    uint64_t best = red_best[mrow * Cfg::WN];
+    float lm = red_m[mrow * Cfg::WN], ls = red_s[mrow * Cfg::WN];
+    for (int q = 1; q < Cfg::WN; ++q) {
+      best = umax64(best, red_best[mrow * Cfg::WN + q]);
+      const float m2 = red_m[mrow * Cfg::WN + q];
+      if (m2 != -__builtin_huge_valf()) {
+        if (lm == -__builtin_huge_valf()) { lm = m2; ls = red_s[mrow * Cfg::WN + q]; }
+        else lse_merge(lm, ls, m2, red_s[mrow * Cfg::WN + q]);
+      }
+    }
+    const size_t o = (size_t)m * a.ntiles + nt;
+    a.part_best[o] = best;
+    a.part_m[o] = lm;
+    a.part_s[o] = ls;
+  }
+}
+
+// One wavefront per row: merge the row's tile partials (strided by lane, then a fixed xor tree).
+__global__ __launch_bounds__(64) void lmhead_finalize(const uint64_t* part_best, const float* part_m, const float* part_s,
+                                                      int ntiles, int32_t* token, float* lse) {
+  const int row = blockIdx.x, lane = threadIdx.x;
+  uint64_t best = 0;
+  float lm = -__builtin_huge_valf(), ls = 0.0f;
+  for (int t = lane; t < ntiles; t += 64) {
+    const size_t o = (size_t)row * ntiles + t;
+    best = umax64(best, part_best[o]);
+    const float m2 = part_m[o];
+    if (m2 != -__builtin_huge_valf()) {
+      if (lm == -__builtin_huge_valf()) { lm = m2; ls = part_s[o]; }
+      else lse_merge(lm, ls, m2, part_s[o]);
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    best = umax64(best, shfl_xor_u64(best, off));
+    const float m2 = shfl_xor_f(lm, off), s2 = shfl_xor_f(ls, off);
+    if (m2 != -__builtin_huge_valf()) {
+      if (lm == -__builtin_huge_valf()) { lm = m2; ls = s2; }
+      else lse_merge(lm, ls, m2, s2);
+    }
+  }
+  if (lane == 0) {
+    token[row] = unpack_idx(best);
+    if (lse) lse[row] = lm + logf(ls);
+  }
+}
+
+template <typename T, typename Cfg>
+int32_t launch(LmArgs& a, hipStream_t st) {
+  const int mtiles = (a.M + Cfg::BM - 1) / Cfg::BM;
+  const size_t lds = std::max(Cfg::LDS_BYTES, (size_t)Cfg::BM * Cfg::WN * 16);
+  hipLaunchKernelGGL((lmhead_kernel<T, Cfg>), dim3(mtiles * a.ntiles), dim3(256), lds, st, a);
+  return check_launch("orthrus_lmhead_argmax");
+}
+
+constexpr int kLmBN = 128;
+
+}  // namespace
+}  // namespace orthrus
+
+using namespace orthrus;
+
+extern "C" size_t orthrus_lmhead_workspace_bytes(const orthrus_lmhead_desc_t* d) {
+  if (!d || d->rows < 0 || d->vocab <= 0) return 0;
+  const size_t ntiles = (d->vocab + kLmBN - 1) / kLmBN;
+  return (size_t)d->rows * ntiles * (sizeof(uint64_t) + 2 * sizeof(float));
+}
+
+extern "C" int32_t orthrus_lmhead_argmax(const orthrus_lmhead_desc_t* d, const void* h, const void* w,
+                                         const int32_t* seq_id, const int32_t* round, int32_t* token_out,
+                                         float* logits_out, float* lse_out, void* ws, size_t ws_bytes, void* stream) {
+  ORTHRUS_REQUIRE(d != nullptr, ORTHRUS_ERR_INVALID_ARG, "lmhead: null descriptor");
+  ORTHRUS_REQUIRE(d->rows >= 0 && d->hidden > 0 && d->vocab > 0, ORTHRUS_ERR_INVALID_ARG, "lmhead: bad sizes");
+  ORTHRUS_REQUIRE(d->hidden % 64 == 0, ORTHRUS_ERR_UNSUPPORTED, "lmhead: hidden %d not a multiple of 64", d->hidden);
+  ORTHRUS_REQUIRE(valid_dtype(d->dtype), ORTHRUS_ERR_INVALID_ARG, "lmhead: bad dtype");
+  ORTHRUS_REQUIRE(d->temperature >= 0.0f && std::isfinite(d->temperature), ORTHRUS_ERR_INVALID_ARG,
+                  "lmhead: temperature must be finite and >= 0");
+  ORTHRUS_REQUIRE(h && w && token_out, ORTHRUS_ERR_INVALID_ARG, "lmhead: null pointer");
+  const bool sample = d->temperature > 0.0f;
+  ORTHRUS_REQUIRE(!sample || (seq_id && round && d->block > 0 && d->rows % d->block == 0), ORTHRUS_ERR_INVALID_ARG,
+                  "lmhead: sampling needs seq_id, round and rows %% block == 0");
+  const size_t need = orthrus_lmhead_workspace_bytes(d);
+  ORTHRUS_REQUIRE(ws && ws_bytes >= need, ORTHRUS_ERR_WORKSPACE, "lmhead: workspace %zu < %zu", ws_bytes, need);
+  if (d->rows == 0) return ORTHRUS_OK;
+  LmArgs a;
+  a.h = h; a.w = w; a.seq_id = seq_id; a.round = round; a.logits = logits_out;
+  a.M = d->rows; a.N = d->vocab; a.K = d->hidden; a.block = d->block > 0 ? d->block : 1;
+  a.ntiles = (d->vocab + kLmBN - 1) / kLmBN;
+  a.part_best = reinterpret_cast<uint64_t*>(ws);
+  a.part_m = reinterpret_cast<float*>(a.part_best + (size_t)a.M * a.ntiles);
+  a.part_s = a.part_m + (size_t)a.M * a.ntiles;
+  a.inv_t = sample ? 1.0f / d->temperature : 1.0f;
+  a.sample = sample;
+  a.seed = d->seed;
+  a.stream_id = (uint64_t)d->stream_id;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  int32_t s;
+  if (d->dtype == ORTHRUS_BF16) {
+    if (a.M <= 32) s = launch<bf16, GemmCfg<bf16, 32, kLmBN, 1, 4>>(a, st);
+    else if (a.M <= 64) s = launch<bf16, GemmCfg<bf16, 64, kLmBN, 2, 2>>(a, st);
+    else s = launch<bf16, GemmCfg<bf16, 128, kLmBN, 2, 2>>(a, st);
+  } else {
+    if (a.M <= 32) s = launch<float, GemmCfg<float, 32, kLmBN, 1, 4>>(a, st);
+    else if (a.M <= 64) s = launch<float, GemmCfg<float, 64, kLmBN, 2, 2>>(a, st);
+    else s = launch<float, GemmCfg<float, 128, kLmBN, 2, 2>>(a, st);
+  }
+  if (s != ORTHRUS_OK) return s;
+  hipLaunchKernelGGL(lmhead_finalize, dim3(a.M), dim3(64), 0, st, a.part_best, a.part_m, a.part_s, a.ntiles, token_out,
+                     lse_out);
+  return check_launch("orthrus_lmhead_argmax(finalize)");
+}

@@ -1,0 +1,303 @@
+"""Round driver: prefill, Orthrus rounds (draft pass, verify pass, consensus/commit) and the
+plain AR reference, all through the C ABI on device-resident state.
+
+Orthrus paper summary (cjcn.com.cn), sec. 二: the frozen AR model owns the only KV cache and
+the diffusion view reads it; sec. 四: one round = a parallel draft pass over the anchor and
+[MASK] slots, one causal AR pass over the block with the drafts filled in, then left-to-right
+consensus (strict rejection sampling at temperature > 0).
+
+Every arithmetic step runs in liborthrus kernels.  PyTorch only allocates device memory and
+provides the stream; the host enqueues launches and never reads round state inside a round,
+so a whole round can be captured once into a HIP graph and replayed.
+"""
+from __future__ import annotations
+
+import dataclasses
+import time
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+@dataclasses.dataclass
+class GenStats:
+    rounds: int
+    tokens: int
+    passes: int
+    decode_s: float
+    accept_hist: list
+
+    @property
+    def tpf(self) -> float:
+        return self.tokens / max(1, self.passes)
+
+    @property
+    def tokens_per_s(self) -> float:
+        return self.tokens / self.decode_s if self.decode_s > 0 else float("nan")
+
+
+class Decoder:
+    """A random-init (or given) decoder with an AR view and a diffusion attention view.
+
+    ``weights``: dict of host float32 arrays in Linear layout (``embed``, ``lm_head``,
+    ``final_norm`` and per layer ``l.attn_norm, l.mlp_norm, l.wq, l.wk, l.wv, l.wo, l.w_gate,
+    l.w_up, l.w_down`` plus the diffusion view's ``l.dq, l.dk, l.dv, l.do``).
+    ``shape``: object with layers, hidden, q_heads, kv_heads, head_dim, inter, vocab,
+    rope_base, eps, mask_id.
+    ``precision``: 'bf16' (bf16 weights and activations, fp32 inside kernels) or 'fp32'.
+    """
+
+    def __init__(self, weights: dict, shape, precision: str = "bf16", block: int = 32, max_batch: int = 1,
+                 max_ctx: int = 4096, page_size: int = 16, kv_chunk: int = 1024, device: str = "cuda",
+                 page_order_seed: int | None = None):
+        L.lib()  # fail loudly if the HIP library is missing
+        self.shape = s = shape
+        self.K = block
+        self.B = max_batch
+        self.dev = torch.device(device)
+        self.prec = precision
+        self.dt = L.BF16 if precision == "bf16" else L.F32
+        self.tdt = torch.bfloat16 if precision == "bf16" else torch.float32
+        self.page = page_size
+        self.kv_chunk = kv_chunk
+        self.max_pages = -(-(max_ctx + block) // page_size)
+        self.max_ctx = self.max_pages * page_size
+        self.max_pos = self.max_ctx + block
+        H, D, Hq, Hkv, I, V = s.hidden, s.head_dim, s.q_heads, s.kv_heads, s.inter, s.vocab
+        self.nqkv = (Hq + 2 * Hkv) * D
+
+        def up(a, dt=None):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dtype=dt or self.tdt, device=self.dev)
+
+        W = weights
+        self.embed = up(W["embed"])
+        self.lm_head = up(W["lm_head"])
+        self.final_norm = up(W["final_norm"], torch.float32)
+        self.layers = []
+        for l in range(s.layers):
+            gate, upw = up(W[f"{l}.w_gate"]), up(W[f"{l}.w_up"])
+            gu = torch.empty((2 * I, H), dtype=self.tdt, device=self.dev)
+            L.pack_gate_up(I, H, self.dt, gate, upw, gu)
+            del gate, upw
+            self.layers.append(dict(
+                attn_norm=up(W[f"{l}.attn_norm"], torch.float32),
+                mlp_norm=up(W[f"{l}.mlp_norm"], torch.float32),
+                qkv_ar=up(np.concatenate([W[f"{l}.wq"], W[f"{l}.wk"], W[f"{l}.wv"]])),
+                o_ar=up(W[f"{l}.wo"]),
+                qkv_diff=up(np.concatenate([W[f"{l}.dq"], W[f"{l}.dk"], W[f"{l}.dv"]])),
+                o_diff=up(W[f"{l}.do"]),
+                gate_up=gu,
+                down=up(W[f"{l}.w_down"]),
+            ))
+        torch.cuda.synchronize(self.dev)
+        # paged AR cache (the only cache), one pool per layer
+        self.num_pages = self.B * self.max_pages
+        self.k_pages = [torch.zeros((self.num_pages, Hkv, page_size, D), dtype=self.tdt, device=self.dev)
+                        for _ in range(s.layers)]
+        self.v_pages = [torch.zeros_like(k) for k in self.k_pages]
+        order = np.arange(self.num_pages, dtype=np.int32)
+        if page_order_seed is not None:
+            order = np.random.default_rng(page_order_seed).permutation(self.num_pages).astype(np.int32)
+        self.page_table = torch.from_numpy(order.reshape(self.B, self.max_pages)).to(self.dev)
+        self.rope = torch.empty((self.max_pos, D // 2, 2), dtype=torch.float32, device=self.dev)
+        L.rope_table(self.max_pos, D, float(s.rope_base), self.rope)
+        # activations for up to B*K rows
+        M = self.B * block
+        self.x = torch.empty((M, H), dtype=self.tdt, device=self.dev)
+        self.a = torch.empty_like(self.x)
+        self.qkv = torch.empty((M, self.nqkv), dtype=self.tdt, device=self.dev)
+        self.q = torch.empty((M, Hq * D), dtype=self.tdt, device=self.dev)
+        self.o = torch.empty((M, Hq * D), dtype=self.tdt, device=self.dev)
+        self.h = torch.empty((M, I), dtype=self.tdt, device=self.dev)
+        self.k_blk = torch.empty((self.B, block, Hkv, D), dtype=self.tdt, device=self.dev)
+        self.v_blk = torch.empty_like(self.k_blk)
+        self.attn_ws = {}
+        self.lm_ws = torch.empty(L.lmhead_workspace_bytes(L.lmhead_desc(M, H, V, self.dt)), dtype=torch.uint8,
+                                 device=self.dev)
+        # round state
+        z = lambda: torch.zeros(self.B, dtype=torch.int32, device=self.dev)
+        self.ctx_len, self.anchor, self.accept, self.out_len, self.round, self.done = z(), z(), z(), z(), z(), z()
+        self.seq_id = torch.arange(self.B, dtype=torch.int32, device=self.dev)
+        self.draft = torch.zeros((self.B, block), dtype=torch.int32, device=self.dev)
+        self.target = torch.zeros_like(self.draft)
+        self.out_tokens = None
+        self.max_out = 0
+        self._logits = None
+        self.graph = None
+
+    # ------------------------------------------------------------------ building blocks
+    def _attn_desc(self, nb, kb):
+        s = self.shape
+        return L.attn_desc(nb, s.q_heads, s.kv_heads, s.head_dim, kb, self.page, self.max_pages, self.max_ctx,
+                           self.kv_chunk, self.dt, self.dt, 1.0 / float(np.sqrt(s.head_dim)))
+
+    def _ws(self, desc):
+        key = (desc.batch, desc.block)
+        if key not in self.attn_ws:
+            self.attn_ws[key] = torch.empty(max(16, L.attn_workspace_bytes(desc)), dtype=torch.uint8,
+                                            device=self.dev)
+        return self.attn_ws[key]
+
+    def _layers(self, view: str, nb: int, kb: int, ctx, draft: bool):
+        """Decoder layers over nb*kb rows in self.x (in place); K/V to the cache unless draft."""
+        s = self.shape
+        M = nb * kb
+        H, D, Hq, Hkv, I = s.hidden, s.head_dim, s.q_heads, s.kv_heads, s.inter
+        dt = self.dt
+        desc = self._attn_desc(nb, kb)
+        ws = self._ws(desc)
+        x, a = self.x[:M], self.a[:M]
+        for l, Wl in enumerate(self.layers):
+            L.rmsnorm(M, H, dt, x, Wl["attn_norm"], s.eps, a)
+            L.gemm(M, self.nqkv, H, dt, dt, L.EPI_STORE, a, Wl["qkv_" + view], None, self.qkv)
+            if draft:
+                L.rope_kv_write(nb, kb, Hq, Hkv, D, self.page, self.max_pages, dt, self.qkv, self.rope,
+                                self.max_pos, ctx, None, self.q, self.k_blk, self.v_blk)
+                L.draft_attn(desc, self.q, self.k_pages[l], self.v_pages[l], self.page_table, ctx, self.k_blk,
+                             self.v_blk, self.o, ws)
+            else:
+                L.rope_kv_write(nb, kb, Hq, Hkv, D, self.page, self.max_pages, dt, self.qkv, self.rope,
+                                self.max_pos, ctx, self.page_table, self.q, self.k_pages[l], self.v_pages[l])
+                L.verify_attn(desc, self.q, self.k_pages[l], self.v_pages[l], self.page_table, ctx, self.o, ws)
+            L.gemm(M, H, Hq * D, dt, dt, L.EPI_RESIDUAL, self.o, Wl["o_" + view], x, x)
+            L.rmsnorm(M, H, dt, x, Wl["mlp_norm"], s.eps, a)
+            L.gemm(M, 2 * I, H, dt, dt, L.EPI_SWIGLU, a, Wl["gate_up"], None, self.h)
+            L.gemm(M, H, I, dt, dt, L.EPI_RESIDUAL, self.h, Wl["down"], x, x)
+
+    def _lm_head(self, nb, kb, tokens, temperature=0.0, seed=0, stream_id=L.STREAM_DRAFT, logits=None, lse=None):
+        s = self.shape
+        M = nb * kb
+        L.rmsnorm(M, s.hidden, self.dt, self.x[:M], self.final_norm, s.eps, self.a[:M])
+        d = L.lmhead_desc(M, s.hidden, s.vocab, self.dt, kb, stream_id, temperature, seed)
+        L.lmhead_argmax(d, self.a[:M], self.lm_head, self.seq_id, self.round, tokens, logits, lse, self.lm_ws)
+
+    # ------------------------------------------------------------------ prefill / state
+    def prefill(self, prompts: torch.Tensor, max_out: int):
+        """AR prefill of prompts[:, :-1] in K-row causal chunks; anchor := prompts[:, -1]."""
+        B, P = prompts.shape
+        assert B == self.B and P >= 1 and P - 1 + self.K <= self.max_ctx
+        prompts = prompts.to(self.dev, torch.int32).contiguous()
+        for c in range(0, P - 1, self.K):
+            kb = min(self.K, P - 1 - c)
+            ctx = torch.full((B,), c, dtype=torch.int32, device=self.dev)
+            L.embed_block(B, kb, self.shape.hidden, self.dt, self.embed, None, prompts, P, c, self.shape.mask_id,
+                          self.x)
+            self._layers("ar", B, kb, ctx, draft=False)
+        self.ctx_len.fill_(P - 1)
+        self.anchor.copy_(prompts[:, P - 1])
+        for t in (self.accept, self.out_len, self.round, self.done):
+            t.zero_()
+        if self.out_tokens is None or self.max_out != max_out:
+            # a new buffer: any graph captured against the old one must be captured again
+            self.out_tokens = torch.full((B, max_out), -1, dtype=torch.int32, device=self.dev)
+        else:
+            self.out_tokens.fill_(-1)
+        self.max_out = max_out
+
+    # ------------------------------------------------------------------ one round
+    def round_greedy(self):
+        B, K, s = self.B, self.K, self.shape
+        L.embed_block(B, K, s.hidden, self.dt, self.embed, self.anchor, None, 0, 0, s.mask_id, self.x)
+        self._layers("diff", B, K, self.ctx_len, draft=True)
+        self._lm_head(B, K, self.draft)
+        L.embed_block(B, K, s.hidden, self.dt, self.embed, self.anchor, self.draft, K, 0, s.mask_id, self.x)
+        self._layers("ar", B, K, self.ctx_len, draft=False)
+        self._lm_head(B, K, self.target)
+        L.consensus_commit(B, K, self.draft, self.target, self.ctx_len, self.anchor, self.accept, self.out_tokens,
+                           self.out_len, self.round, self.done, self.max_out, self.max_ctx)
+
+    def round_sampled(self, temperature: float, seed: int):
+        B, K, s = self.B, self.K, self.shape
+        if self._logits is None:
+            M = B * K
+            self._logits = [torch.empty((M, s.vocab), dtype=torch.float32, device=self.dev) for _ in range(2)]
+            self._lse = [torch.empty(M, dtype=torch.float32, device=self.dev) for _ in range(2)]
+        L.embed_block(B, K, s.hidden, self.dt, self.embed, self.anchor, None, 0, 0, s.mask_id, self.x)
+        self._layers("diff", B, K, self.ctx_len, draft=True)
+        self._lm_head(B, K, self.draft, temperature, seed, L.STREAM_DRAFT, self._logits[0], self._lse[0])
+        L.embed_block(B, K, s.hidden, self.dt, self.embed, self.anchor, self.draft, K, 0, s.mask_id, self.x)
+        self._layers("ar", B, K, self.ctx_len, draft=False)
+        self._lm_head(B, K, self.target, temperature, seed, L.STREAM_AR, self._logits[1], self._lse[1])
+        L.rejection_accept(B, K, s.vocab, temperature, seed, self.seq_id, self._logits[0], self._logits[1],
+                           self._lse[0], self._lse[1], self.draft, self.ctx_len, self.anchor, self.accept,
+                           self.out_tokens, self.out_len, self.round, self.done, self.max_out, self.max_ctx)
+
+    def ar_step(self, temperature: float = 0.0, seed: int = 0):
+        """One plain AR step for every sequence: a one-row causal pass, argmax/sample, commit."""
+        B, s = self.B, self.shape
+        L.embed_block(B, 1, s.hidden, self.dt, self.embed, self.anchor, None, 0, 0, s.mask_id, self.x)
+        self._layers("ar", B, 1, self.ctx_len, draft=False)
+        tok = self.target[:, :1]
+        t_flat = self.target.view(-1)[:B]
+        self._lm_head(B, 1, t_flat, temperature, seed, L.STREAM_AR)
+        L.consensus_commit(B, 1, t_flat, t_flat, self.ctx_len, self.anchor, self.accept, self.out_tokens,
+                           self.out_len, self.round, self.done, self.max_out, self.max_ctx)
+        return tok
+
+    # ------------------------------------------------------------------ graphs
+    def capture(self, fn, *args):
+        """Capture one call of ``fn`` (a round or AR step) into a HIP graph."""
+        st = torch.cuda.Stream(device=self.dev)
+        st.wait_stream(torch.cuda.current_stream(self.dev))
+        with torch.cuda.stream(st):
+            fn(*args)  # warm-up: allocates attention workspaces outside the capture
+        torch.cuda.current_stream(self.dev).wait_stream(st)
+        torch.cuda.synchronize(self.dev)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn(*args)
+        return g
+
+    # ------------------------------------------------------------------ drivers
+    def generate(self, prompts, max_new: int, temperature: float = 0.0, seed: int = 0, use_graph: bool = False,
+                 poll_every: int = 8, record_accepts: bool = False, max_rounds: int | None = None):
+        """Orthrus decoding; returns (tokens [B, max_new] int32 numpy, GenStats)."""
+        self.prefill(torch.as_tensor(prompts), max_new)
+        torch.cuda.synchronize(self.dev)
+        fn, args = (self.round_greedy, ()) if temperature == 0.0 else (self.round_sampled, (temperature, seed))
+        hist = []
+        t0 = time.perf_counter()
+        if use_graph:
+            # graph capture runs the round once more during warm-up; redo prefill state after capture
+            g = self.capture(fn, *args)
+            self.prefill(torch.as_tensor(prompts), max_new)
+            torch.cuda.synchronize(self.dev)
+            t0 = time.perf_counter()
+        rounds = 0
+        while True:
+            for _ in range(poll_every):
+                if use_graph:
+                    g.replay()
+                else:
+                    fn(*args)
+                rounds += 1
+                if record_accepts:
+                    hist.append(self.accept.cpu().numpy().copy())
+            if bool((self.done != 0).all()) or (max_rounds is not None and rounds >= max_rounds):
+                break
+        torch.cuda.synchronize(self.dev)
+        dt = time.perf_counter() - t0
+        toks = self.out_tokens.cpu().numpy()
+        nround = self.round.cpu().numpy()
+        stats = GenStats(int(nround.max()), int(self.out_len.sum().item()), 2 * int(nround.sum()), dt, hist)
+        return toks, stats
+
+    def generate_ar(self, prompts, max_new: int, temperature: float = 0.0, seed: int = 0, use_graph: bool = False):
+        """Plain AR decoding through the same kernels (one causal row per step)."""
+        self.prefill(torch.as_tensor(prompts), max_new)
+        torch.cuda.synchronize(self.dev)
+        if use_graph:
+            g = self.capture(self.ar_step, temperature, seed)
+            self.prefill(torch.as_tensor(prompts), max_new)
+            torch.cuda.synchronize(self.dev)
+        t0 = time.perf_counter()
+        for _ in range(max_new):
+            if use_graph:
+                g.replay()
+            else:
+                self.ar_step(temperature, seed)
+        torch.cuda.synchronize(self.dev)
+        dt = time.perf_counter() - t0
+        return self.out_tokens.cpu().numpy(), GenStats(max_new, self.B * max_new, max_new, dt, [])

@@ -1,0 +1,68 @@
+"""The C-ABI library loads on the CPU and exports every symbol the header declares.
+
+No compute call is made here (no GPU in this process): only entry points that answer from
+host-side validation before touching the device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import orthrus_round_amd as ora
+from orthrus_round_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "orthrus.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int32_t|size_t|const char\*)\s+(orthrus_[a-z0-9_]+)\(", text, re.M)))
+
+
+def test_header_symbols_exported_and_bound():
+    L = ora.lib()
+    names = _declared()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_lib.EXPORTED)
+
+
+def test_abi_version_matches_header():
+    m = re.search(r"#define ORTHRUS_ABI_VERSION (\d+)", open(HEADER).read())
+    assert ora.abi_version() == int(m.group(1))
+
+
+def test_struct_layouts_match_header():
+    # orthrus_attn_desc_t: 11 int32 + float; orthrus_lmhead_desc_t: 6 int32 + float + pad + uint64
+    assert ctypes.sizeof(_lib.AttnDesc) == 48
+    assert ctypes.sizeof(_lib.LmHeadDesc) == 40 and _lib.LmHeadDesc.seed.offset == 32
+
+
+@pytest.mark.parametrize("call,status", [
+    (lambda: ora.gemm(4, 64, 63, ora.BF16, ora.BF16, 0, 1, 1, None, 1, stream=0), 2),
+    (lambda: ora.gemm(4, 64, 64, ora.BF16, ora.BF16, 1, 1, 1, None, 1, stream=0), 1),
+    (lambda: ora.gemm(4, 64, 64, ora.F32, ora.BF16, 0, 1, 1, None, 1, stream=0), 2),
+    (lambda: ora.consensus_commit(2, 33, 1, 1, 1, 1, 1, 1, 1, 1, 1, 8, 64, stream=0), 1),
+    (lambda: ora.rmsnorm(2, 64, 7, 1, 1, 1e-6, 1, stream=0), 1),
+    (lambda: ora.rope_table(0, 64, 1e6, 1, stream=0), 1),
+])
+def test_validation_errors_before_launch(call, status):
+    with pytest.raises(ora.OrthrusError) as e:
+        call()
+    assert e.value.status == status
+    assert ora.lib().orthrus_last_error()
+
+
+def test_attention_descriptor_validation():
+    d = ora.attn_desc(1, 16, 8, 128, 32, 16, 4, 64, kv_chunk=0)
+    assert ora.attn_workspace_bytes(d) == 0  # one chunk at max_ctx 64
+    d2 = ora.attn_desc(2, 32, 8, 128, 32, 16, 1100, 17600, kv_chunk=1024)
+    assert ora.attn_workspace_bytes(d2) == 2 * 8 * 18 * 4 * 32 * 130 * 4
+    bad = [ora.attn_desc(1, 12, 8, 128, 32, 16, 4, 64), ora.attn_desc(1, 16, 8, 96, 32, 16, 4, 64),
+           ora.attn_desc(1, 16, 8, 128, 33, 16, 4, 64), ora.attn_desc(1, 16, 8, 128, 32, 16, 4, 65),
+           ora.attn_desc(1, 16, 8, 128, 32, 16, 4, 64, kv_chunk=48), ora.attn_desc(1, 24, 8, 128, 32, 16, 4, 64)]
+    for d in bad:
+        with pytest.raises(ora.OrthrusError):
+            ora.verify_attn(d, 1, 1, 1, 1, 1, 1, None, stream=0)

@@ -1,0 +1,379 @@
+"""GPU parity of the LM head, consensus/commit, rejection accept, Philox and the support
+kernels (C ABI) against the CPU oracle.
+
+Bars: token ids, accept counts, corrections and KV lengths bit-exact, except argmax rows
+whose oracle top-2 gap is below eps_tie = 1e-4 * max(1, |z_top|) (either id passes; such
+rows are counted and printed); float outputs within 2e-3 normwise (bf16) / 2e-5 (fp32).
+"""
+import numpy as np
+import pytest
+import torch
+
+import orthrus_round_amd as ora
+import synth
+from oracle import decode as Dc
+from oracle import model as M
+from oracle import philox as P
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def dev(x, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if dtype == ora.BF16:
+        t = t.to(torch.bfloat16)
+    return t.to(DEV)
+
+
+def tie_ok(z, gpu_id, ref_id):
+    """Same id, or an oracle near-tie between the two ids."""
+    if gpu_id == ref_id:
+        return True, False
+    gap = z[ref_id] - z[gpu_id]
+    return gap <= 1e-4 * max(1.0, abs(z[ref_id])), True
+
+
+def lmhead(h, w, dtype, temperature=0.0, seed=0, block=32, seq=None, rnd=None, want_logits=False):
+    rows, hidden = h.shape
+    vocab = w.shape[0]
+    d = ora.lmhead_desc(rows, hidden, vocab, dtype, block, ora.STREAM_DRAFT, temperature, seed)
+    ws = torch.empty(ora.lmhead_workspace_bytes(d), dtype=torch.uint8, device=DEV)
+    tok = torch.full((rows,), -7, dtype=torch.int32, device=DEV)
+    lse = torch.empty(rows, dtype=torch.float32, device=DEV)
+    logits = torch.empty((rows, vocab), dtype=torch.float32, device=DEV) if want_logits else None
+    nb = rows // block
+    seq_t = dev(np.arange(nb, dtype=np.int32) if seq is None else seq)
+    rnd_t = dev(np.zeros(nb, np.int32) if rnd is None else rnd)
+    ora.lmhead_argmax(d, dev(h, dtype), dev(w, dtype), seq_t, rnd_t, tok, logits, lse, ws)
+    torch.cuda.synchronize()
+    return tok.cpu().numpy(), lse.cpu().numpy(), (logits.cpu().numpy() if want_logits else None)
+
+
+# ------------------------------------------------------------------- LM head
+
+@pytest.mark.parametrize("rows,hidden,vocab,dtype", [(64, 256, 4096, ora.F32), (37, 256, 4000, ora.BF16),
+                                                     (128, 512, 1024 + 64, ora.BF16), (8, 4096, 8192, ora.BF16)])
+def test_lmhead_argmax_small(rows, hidden, vocab, dtype):
+    h, w = synth.lmhead_inputs(8, rows, hidden, vocab, bf16=(dtype == ora.BF16))
+    tok, lse, logits = lmhead(h, w, dtype, block=1, want_logits=True)
+    z = h.astype(np.float64) @ w.astype(np.float64).T
+    ref = M.argmax_lowest(z)
+    amb = 0
+    for r in range(rows):
+        ok, a = tie_ok(z[r], tok[r], ref[r])
+        assert ok, (r, tok[r], ref[r])
+        amb += a
+    tol = 2e-5 if dtype == ora.F32 else 2e-3
+    assert np.abs(logits - z).max() / np.abs(z).max() <= tol
+    zl = z.max(1) + np.log(np.exp(z - z.max(1, keepdims=True)).sum(1))
+    np.testing.assert_allclose(lse, zl, rtol=1e-5, atol=1e-5)
+    print("ambiguous rows:", amb)
+
+
+def test_lmhead_exact_ties_lowest_id():
+    rs = np.random.default_rng(3)
+    w = synth.bf16_round(rs.standard_normal((2048, 128)).astype(np.float32))
+    w[1500] = w[100]
+    w[1900] = w[100]
+    h = synth.bf16_round((w[100:101] * 2).astype(np.float32))
+    tok, _, _ = lmhead(np.repeat(h, 4, 0), w, ora.BF16, block=1)
+    assert (tok == 100).all()
+
+
+@pytest.fixture(scope="module")
+def c4():
+    h, w = synth.lmhead_inputs(4, 512, 4096, 151936)
+    return h, w
+
+
+def test_lmhead_qwen3_8b_sampled_rows(c4):
+    h, w = c4
+    tok, lse, _ = lmhead(h, w, ora.BF16)
+    rows = np.random.default_rng(5).choice(512, 48, replace=False)
+    z = h[rows].astype(np.float64) @ w.astype(np.float64).T
+    ref = M.argmax_lowest(z)
+    for i, r in enumerate(rows):
+        assert tie_ok(z[i], tok[r], ref[i])[0], (r, tok[r], ref[i])
+    zl = z.max(1) + np.log(np.exp(z - z.max(1, keepdims=True)).sum(1))
+    np.testing.assert_allclose(lse[rows], zl, rtol=1e-5)
+
+
+def test_lmhead_row_invariance(c4):
+    """A row's token does not depend on how many rows share the launch."""
+    h, w = c4
+    full = lmhead(h[:64], w, ora.BF16, block=1)
+    for m in (1, 7, 32):
+        part = lmhead(h[:m], w, ora.BF16, block=1)
+        assert np.array_equal(part[0], full[0][:m])
+        np.testing.assert_allclose(part[1], full[1][:m], rtol=1e-6)  # lse merge order follows the tile shape
+
+
+def test_lmhead_gumbel_sampling_matches_oracle():
+    T, seed = 0.8, 1234
+    h, w = synth.lmhead_inputs(9, 64, 256, 4096, bf16=False)
+    seqs = np.array([5, 9], np.int32)
+    rnds = np.array([3, 0], np.int32)
+    tok, lse, _ = lmhead(h, w, ora.F32, temperature=T, seed=seed, block=32, seq=seqs, rnd=rnds)
+    z = h.astype(np.float64) @ w.astype(np.float64).T
+    amb = 0
+    for r in range(64):
+        b, s = divmod(r, 32)
+        u = P.uniforms(seed, P.STREAM_DRAFT, s, np.arange(4096), rnds[b], seqs[b])
+        key = z[r] / T - np.log(-np.log(u))
+        ok, a = tie_ok(key, tok[r], int(np.argmax(key)))
+        assert ok, r
+        amb += a
+    zt = z / T
+    np.testing.assert_allclose(lse, zt.max(1) + np.log(np.exp(zt - zt.max(1, keepdims=True)).sum(1)), rtol=1e-5)
+
+
+def test_lmhead_sampling_distribution_tiny_vocab():
+    """Gumbel-max on device draws from softmax(z/T): chi-square over many (round) counters."""
+    V, T = 64, 0.8
+    rs = np.random.default_rng(11)
+    w = (rs.standard_normal((V, 64)) * 0.3).astype(np.float32)
+    h = np.ones((32, 64), np.float32)
+    z = (h[0].astype(np.float64) @ w.T.astype(np.float64))
+    p = np.exp(z / T - (z / T).max())
+    p /= p.sum()
+    counts = np.zeros(V)
+    for rnd in range(200):
+        tok, _, _ = lmhead(h, w, ora.F32, temperature=T, seed=77, block=32, rnd=np.array([rnd], np.int32))
+        counts += np.bincount(tok, minlength=V)
+    N = counts.sum()
+    mask = p * N >= 5
+    chi2 = ((counts[mask] - N * p[mask]) ** 2 / (N * p[mask])).sum()
+    assert chi2 < mask.sum() + 6 * np.sqrt(2 * mask.sum())
+
+
+# ------------------------------------------------------------------- consensus / commit
+
+def test_consensus_commit_geometric_drafts(c4):
+    h, w = c4
+    t, _, _ = lmhead(h, w, ora.BF16)
+    t = t.reshape(16, 32)
+    d, L = synth.geometric_drafts(4, t, 151936)
+    ctx0 = synth.ragged_lengths(4, 16, 512, 16384)
+    max_out, max_ctx = 40, 20000
+    st = {k: torch.zeros(16, dtype=torch.int32, device=DEV) for k in ("anchor", "accept", "out_len", "round", "done")}
+    ctx = dev(ctx0)
+    out = torch.full((16, max_out), -1, dtype=torch.int32, device=DEV)
+    st["out_len"][:3] = torch.tensor([0, 20, 39], dtype=torch.int32)
+    st["done"][15] = 1
+    ora.consensus_commit(16, 32, dev(d), dev(t), ctx, st["anchor"], st["accept"], out, st["out_len"], st["round"],
+                         st["done"], max_out, max_ctx)
+    torch.cuda.synchronize()
+    acc, ol, an, cx = (st["accept"].cpu().numpy(), st["out_len"].cpu().numpy(), st["anchor"].cpu().numpy(),
+                       ctx.cpu().numpy())
+    outn = out.cpu().numpy()
+    ol0 = np.array([0, 20, 39] + [0] * 13)
+    for b in range(15):
+        k, em = Dc.consensus(d[b], t[b])
+        assert acc[b] == k == L[b]
+        assert cx[b] == ctx0[b] + min(k + 1, 32)
+        assert an[b] == em[-1]
+        wr = min(len(em), max_out - ol0[b])
+        assert ol[b] == ol0[b] + wr
+        assert list(outn[b, ol0[b]:ol0[b] + wr]) == em[:wr]
+    assert acc[15] == -1 and cx[15] == ctx0[15] and ol[15] == 0
+    dn = st["done"].cpu().numpy()
+    assert dn[2] == 1 and dn[15] == 1
+
+
+def test_consensus_every_mismatch_position():
+    K = 32
+    B = K + 1
+    rs = np.random.default_rng(2)
+    t = rs.integers(0, 1000, size=(B, K)).astype(np.int32)
+    d = t.copy()
+    for b in range(K):
+        d[b, b] = (t[b, b] + 1) % 1000
+    st = {k: torch.zeros(B, dtype=torch.int32, device=DEV) for k in ("anchor", "accept", "out_len", "round", "done")}
+    ctx = torch.full((B,), 100, dtype=torch.int32, device=DEV)
+    out = torch.full((B, 64), -1, dtype=torch.int32, device=DEV)
+    ora.consensus_commit(B, K, dev(d), dev(t), ctx, st["anchor"], st["accept"], out, st["out_len"], st["round"],
+                         st["done"], 64, 100000)
+    acc = st["accept"].cpu().numpy()
+    assert list(acc) == list(range(K)) + [K]
+    assert list(ctx.cpu().numpy()) == [100 + min(k + 1, K) for k in range(K + 1)]
+    assert (st["round"].cpu().numpy() == 1).all()
+
+
+# ------------------------------------------------------------------- rejection accept
+
+@pytest.mark.parametrize("V,mix", [(1000, 0.9), (4096, 0.99), (151936, 0.9)])
+def test_rejection_accept_matches_oracle(V, mix):
+    B, K, T, seed = 8, 32, 0.8, 4242
+    ht, w = synth.lmhead_inputs(12, B * K, 256, V, bf16=False)
+    hd = synth.draft_hidden(12, ht, mix=mix, bf16=False)
+    seqs = np.arange(B, dtype=np.int32) * 3 + 1
+    rnds = np.arange(B, dtype=np.int32)
+    # draft logits with their lse, target logits with theirs
+    dd = ora.lmhead_desc(B * K, 256, V, ora.F32, K, ora.STREAM_DRAFT, T, seed)
+    ws = torch.empty(ora.lmhead_workspace_bytes(dd), dtype=torch.uint8, device=DEV)
+    zt_t = torch.empty((B * K, V), dtype=torch.float32, device=DEV)
+    zd_t = torch.empty((B * K, V), dtype=torch.float32, device=DEV)
+    lt, ld = (torch.empty(B * K, dtype=torch.float32, device=DEV) for _ in range(2))
+    tt, dt = (torch.empty(B * K, dtype=torch.int32, device=DEV) for _ in range(2))
+    ora.lmhead_argmax(dd, dev(ht), dev(w), dev(seqs), dev(rnds), tt, zt_t, lt, ws)
+    ora.lmhead_argmax(dd, dev(hd), dev(w), dev(seqs), dev(rnds), dt, zd_t, ld, ws)
+    st = {k: torch.zeros(B, dtype=torch.int32, device=DEV) for k in ("anchor", "accept", "out_len", "done")}
+    rnd_t = dev(rnds.copy())
+    ctx = torch.full((B,), 500, dtype=torch.int32, device=DEV)
+    out = torch.full((B, 64), -1, dtype=torch.int32, device=DEV)
+    ora.rejection_accept(B, K, V, T, seed, dev(seqs), zd_t, zt_t, ld, lt, dt, ctx, st["anchor"], st["accept"], out,
+                         st["out_len"], rnd_t, st["done"], 64, 100000)
+    torch.cuda.synchronize()
+    acc = st["accept"].cpu().numpy()
+    outn = out.cpu().numpy()
+    dtn = dt.cpu().numpy().reshape(B, K)
+    zdn = zd_t.cpu().numpy().astype(np.float64).reshape(B, K, V)
+    ztn = zt_t.cpu().numpy().astype(np.float64).reshape(B, K, V)
+    for b in range(B):
+        ua = P.uniforms(seed, P.STREAM_ACCEPT, np.arange(K), 0, rnds[b], seqs[b])
+        er = -np.log(P.uniforms(seed, P.STREAM_RESID, np.arange(V), 0, rnds[b], seqs[b]))
+        k, em = Dc.rejection_accept(zdn[b], ztn[b], dtn[b], T, ua, er)
+        assert acc[b] == k, (b, acc[b], k)
+        assert list(outn[b, :len(em)]) == em, b
+    assert (rnd_t.cpu().numpy() == rnds + 1).all()
+    assert (ctx.cpu().numpy() == 500 + np.minimum(acc + 1, K)).all()
+
+
+# ------------------------------------------------------------------- Philox
+
+def test_philox_words_match_numpy():
+    rs = np.random.default_rng(0)
+    n = 1000
+    ctr = rs.integers(0, 2**63, size=(n, 4), dtype=np.uint64)
+    key = rs.integers(0, 2**63, size=2, dtype=np.uint64)
+    out = torch.empty((n, 4), dtype=torch.int64, device=DEV)
+    ctr_t = torch.from_numpy(ctr.view(np.int64)).to(DEV)
+    ora.philox4x64(n, ctr_t, int(key[0]), int(key[1]), out)
+    got = out.cpu().numpy().view(np.uint64)
+    for i in range(0, n, 97):
+        c = [int(x) for x in ctr[i]]
+        v = (c[0] | (c[1] << 64) | (c[2] << 128) | (c[3] << 192)) - 1
+        v %= 2**256
+        bg = np.random.Philox(key=key, counter=np.array([(v >> (64 * j)) & (2**64 - 1) for j in range(4)],
+                                                        dtype=np.uint64))
+        assert np.array_equal(got[i], bg.random_raw(4))
+
+
+# ------------------------------------------------------------------- support kernels
+
+@pytest.mark.parametrize("dtype", [ora.BF16, ora.F32])
+@pytest.mark.parametrize("M,N,K", [(256, 6144, 4096), (8, 4096, 4096), (45, 1024, 256), (100, 320, 128)])
+@pytest.mark.parametrize("epi", [ora.EPI_STORE, ora.EPI_RESIDUAL, ora.EPI_SWIGLU])
+def test_gemm_epilogues(dtype, M, N, K, epi):
+    if epi == ora.EPI_SWIGLU and N % 64:
+        pytest.skip("SwiGLU needs N % 64 == 0")
+    bf = dtype == ora.BF16
+    a, w = synth.lmhead_inputs(20, M, K, N, h_std=1.0, w_std=0.02, bf16=bf)
+    res = synth.lmhead_inputs(21, M, N, 8, bf16=bf)[0] if epi == ora.EPI_RESIDUAL else None
+    z = a.astype(np.float64) @ w.astype(np.float64).T
+    if epi == ora.EPI_SWIGLU:
+        ncol = N // 2
+        g = torch.empty((M, ncol), dtype=torch.bfloat16 if bf else torch.float32, device=DEV)
+        packed = torch.empty((N, K), dtype=g.dtype, device=DEV)
+        ora.pack_gate_up(ncol, K, dtype, dev(w[:ncol], dtype), dev(w[ncol:], dtype), packed)
+        ora.gemm(M, N, K, dtype, dtype, epi, dev(a, dtype), packed, None, g)
+        gg, uu = z[:, :ncol], z[:, ncol:]
+        ref = gg / (1 + np.exp(-gg)) * uu
+    else:
+        c = torch.empty((M, N), dtype=torch.bfloat16 if bf else torch.float32, device=DEV)
+        r_t = dev(res, dtype) if res is not None else None
+        if r_t is not None:
+            c.copy_(r_t)  # in place: c aliases the residual
+        ora.gemm(M, N, K, dtype, dtype, epi, dev(a, dtype), dev(w, dtype), c if r_t is not None else None, c)
+        g = c
+        ref = z + (res.astype(np.float64) if res is not None else 0)
+    torch.cuda.synchronize()
+    out = g.float().cpu().numpy()
+    tol = 1e-5 if not bf else 8e-3  # bf16 output rounding
+    assert np.abs(out - ref).max() / np.abs(ref).max() <= tol
+
+
+@pytest.mark.parametrize("dtype", [ora.BF16, ora.F32])
+def test_gemm_row_invariance(dtype):
+    a, w = synth.lmhead_inputs(22, 256, 4096, 1024, bf16=(dtype == ora.BF16))
+    outs = []
+    for m in (256, 64, 32, 1):
+        c = torch.empty((m, 1024), dtype=torch.float32, device=DEV)
+        ora.gemm(m, 1024, 4096, dtype, ora.F32, ora.EPI_STORE, dev(a[:m], dtype), dev(w, dtype), None, c)
+        outs.append(c.cpu().numpy())
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0][: o.shape[0]])
+
+
+@pytest.mark.parametrize("dtype", [ora.BF16, ora.F32])
+def test_rmsnorm(dtype):
+    bf = dtype == ora.BF16
+    x = synth.lmhead_inputs(23, 33, 4096, 8, h_std=3.0, bf16=bf)[0]
+    g = (1 + 0.1 * np.random.default_rng(1).standard_normal(4096)).astype(np.float32)
+    y = torch.empty((33, 4096), dtype=torch.bfloat16 if bf else torch.float32, device=DEV)
+    ora.rmsnorm(33, 4096, dtype, dev(x, dtype), dev(g), 1e-6, y)
+    ref = M.rmsnorm(x.astype(np.float64), g.astype(np.float64), 1e-6)
+    err = np.abs(y.float().cpu().numpy() - ref).max() / np.abs(ref).max()
+    assert err <= (4e-3 if bf else 1e-6)
+
+
+@pytest.mark.parametrize("paged", [True, False])
+@pytest.mark.parametrize("dtype", [ora.BF16, ora.F32])
+def test_rope_kv_write(paged, dtype):
+    B, K, Hq, Hkv, D, page = 3, 32, 8, 2, 128, 16
+    bf = dtype == ora.BF16
+    ctx = np.array([0, 77, 5000], np.int32)
+    qkv = synth.lmhead_inputs(24, B * K, (Hq + 2 * Hkv) * D, 8, bf16=bf)[0]
+    maxpos = 8192
+    table = torch.empty((maxpos, D // 2, 2), dtype=torch.float32, device=DEV)
+    ora.rope_table(maxpos, D, 1e6, table)
+    tdt = torch.bfloat16 if bf else torch.float32
+    q_out = torch.empty((B * K, Hq * D), dtype=tdt, device=DEV)
+    maxp = (5000 + K) // page + 1
+    perm = np.random.default_rng(0).permutation(B * maxp).astype(np.int32).reshape(B, maxp)
+    if paged:
+        kd = torch.full((B * maxp, Hkv, page, D), float("nan"), dtype=tdt, device=DEV)
+        vd = torch.full_like(kd, float("nan"))
+        pt = dev(perm)
+    else:
+        kd = torch.empty((B, K, Hkv, D), dtype=tdt, device=DEV)
+        vd = torch.empty_like(kd)
+        pt = None
+    ora.rope_kv_write(B, K, Hq, Hkv, D, page, maxp, dtype, dev(qkv, dtype), table, maxpos, dev(ctx), pt, q_out, kd, vd)
+    torch.cuda.synchronize()
+    x = qkv.astype(np.float64).reshape(B, K, Hq + 2 * Hkv, D)
+    pos = ctx[:, None] + np.arange(K)[None]
+    rq = M.rope(x[:, :, :Hq], pos[:, :, None], 1e6)
+    rk = M.rope(x[:, :, Hq:Hq + Hkv], pos[:, :, None], 1e6)
+    rv = x[:, :, Hq + Hkv:]
+    tol = 4e-3 if bf else 1e-6
+    assert np.abs(q_out.float().cpu().numpy().reshape(rq.shape) - rq).max() <= tol * np.abs(rq).max()
+    kdn, vdn = kd.float().cpu().numpy(), vd.float().cpu().numpy()
+    for b in range(B):
+        for s in range(K):
+            p = pos[b, s]
+            if paged:
+                gk, gv = kdn[perm[b, p // page], :, p % page], vdn[perm[b, p // page], :, p % page]
+            else:
+                gk, gv = kdn[b, s], vdn[b, s]
+            assert np.abs(gk - rk[b, s]).max() <= tol * np.abs(rk).max()
+            assert np.array_equal(gv, rv[b, s].astype(np.float32)) or bf and np.abs(gv - rv[b, s]).max() < 1e-2
+
+
+def test_embed_block_modes():
+    V, H = 4096, 256
+    E = synth.lmhead_inputs(25, V, H, 8, bf16=False)[0]
+    anchor = np.array([5, 17], np.int32)
+    toks = np.array([[1, 2, 3, 4], [9, 8, 7, 6]], np.int32)
+    Et = dev(E)
+    x = torch.empty((8, H), dtype=torch.float32, device=DEV)
+    ora.embed_block(2, 4, H, ora.F32, Et, dev(anchor), None, 0, 0, V - 1, x)       # draft
+    ref = np.stack([E[5], E[V - 1], E[V - 1], E[V - 1], E[17], E[V - 1], E[V - 1], E[V - 1]])
+    assert np.array_equal(x.cpu().numpy(), ref)
+    ora.embed_block(2, 4, H, ora.F32, Et, dev(anchor), dev(toks), 4, 0, V - 1, x)  # verify
+    ref = np.stack([E[5], E[1], E[2], E[3], E[17], E[9], E[8], E[7]])
+    assert np.array_equal(x.cpu().numpy(), ref)
+    ora.embed_block(2, 2, H, ora.F32, Et, None, dev(toks), 4, 1, V - 1, x[:4])    # prefill chunk
+    ref = np.stack([E[2], E[3], E[8], E[7]])
+    assert np.array_equal(x[:4].cpu().numpy(), ref)
