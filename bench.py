@@ -67,13 +67,13 @@ def kernel_table(dec, ctx_np):
         ms = event_time_ms(fn)
         tab[name] = dict(ms=ms, per_round=per_round, bytes=bytes_, flops=flops)
 
-    add("gemm_qkv", lambda: L.gemm(M, dec.nqkv, H, dt, dt, L.EPI_STORE, dec.a, Wl["qkv_ar"], None, dec.qkv),
+    add("gemm_qkv", lambda: L.gemm(M, dec.nqkv, H, dt, dt, L.EPI_STORE, dec.a, Wl["qkv_ar"], None, dec.qkv, dec.gemm_ws),
         2 * s.layers, (dec.nqkv * H + M * H + M * dec.nqkv) * esz, 2 * M * dec.nqkv * H)
-    add("gemm_o_residual", lambda: L.gemm(M, H, Hq * D, dt, dt, L.EPI_RESIDUAL, dec.o, Wl["o_ar"], dec.x, dec.x),
+    add("gemm_o_residual", lambda: L.gemm(M, H, Hq * D, dt, dt, L.EPI_RESIDUAL, dec.o, Wl["o_ar"], dec.x, dec.x, dec.gemm_ws),
         2 * s.layers, (H * Hq * D + M * Hq * D + 2 * M * H) * esz, 2 * M * H * Hq * D)
-    add("gemm_gate_up_swiglu", lambda: L.gemm(M, 2 * I, H, dt, dt, L.EPI_SWIGLU, dec.a, Wl["gate_up"], None, dec.h),
+    add("gemm_gate_up_swiglu", lambda: L.gemm(M, 2 * I, H, dt, dt, L.EPI_SWIGLU, dec.a, Wl["gate_up"], None, dec.h, dec.gemm_ws),
         2 * s.layers, (2 * I * H + M * H + M * I) * esz, 2 * M * 2 * I * H)
-    add("gemm_down_residual", lambda: L.gemm(M, H, I, dt, dt, L.EPI_RESIDUAL, dec.h, Wl["down"], dec.x, dec.x),
+    add("gemm_down_residual", lambda: L.gemm(M, H, I, dt, dt, L.EPI_RESIDUAL, dec.h, Wl["down"], dec.x, dec.x, dec.gemm_ws),
         2 * s.layers, (H * I + M * I + 2 * M * H) * esz, 2 * M * H * I)
     kv_b = Hkv * D * 2 * esz  # K and V bytes per key
     qo_b = 2 * M * Hq * D * esz

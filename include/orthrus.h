@@ -187,11 +187,16 @@ typedef enum {
                                (see orthrus_pack_gate_up); c[m, j] = silu(g) * u, N/2 columns */
 } orthrus_epilogue_t;
 
-/* c [M, N'] = epilogue(a [M, K] . w [N, K]^T), fp32 accumulation in a fixed k order (the
- * result of an output element never depends on M).  K % 64 == 0, N % 64 == 0. */
+/* c [M, N'] = epilogue(a [M, K] . w [N, K]^T), fp32 accumulation.  K % 64 == 0; SwiGLU needs
+ * N % 64 == 0.  The k-steps of every output tile are split four ways inside one workgroup and
+ * the four partial sums are added in a fixed order, so an output element's bits never depend
+ * on M (a row computed alone equals the same row inside a larger batch).  The workspace
+ * arguments are reserved: orthrus_gemm_workspace_bytes() returns 0 and NULL/0 may be passed. */
+size_t orthrus_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t dtype,
+                                    int32_t epilogue);
 int32_t orthrus_gemm(int32_t M, int32_t N, int32_t K, int32_t dtype, int32_t out_dtype,
                      int32_t epilogue, const void* a, const void* w, const void* residual, void* c,
-                     void* stream);
+                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Interleave gate [I, H] and up [I, H] into [2I, H] in 32-row groups: gate 0..31, up 0..31,
  * gate 32..63, ... (I % 32 == 0). */

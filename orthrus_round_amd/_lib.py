@@ -56,7 +56,8 @@ _SIGS = {
     "orthrus_rejection_workspace_bytes": ([_I32], _SZ),
     "orthrus_rejection_accept": ([_I32, _I32, _I32, _F32, _U64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                   _P, _P, _I32, _I32, _P, _SZ, _P], _I32),
-    "orthrus_gemm": ([_I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P], _I32),
+    "orthrus_gemm_workspace_bytes": ([_I32, _I32, _I32, _I32, _I32], _SZ),
+    "orthrus_gemm": ([_I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P], _I32),
     "orthrus_pack_gate_up": ([_I32, _I32, _I32, _P, _P, _P, _P], _I32),
     "orthrus_rmsnorm": ([_I32, _I32, _I32, _P, _P, _F32, _P, _P], _I32),
     "orthrus_rope_table": ([_I32, _I32, ctypes.c_double, _P, _P], _I32),
@@ -160,8 +161,13 @@ def rejection_accept(batch, block, vocab, temperature, seed, seq_id, draft_logit
                                           _stream(stream)))
 
 
-def gemm(M, N, K, dtype, out_dtype, epilogue, a, w, residual, c, stream=None):
+def gemm_workspace_bytes(M, N, K, dtype, epilogue) -> int:
+    return lib().orthrus_gemm_workspace_bytes(M, N, K, dtype, epilogue)
+
+
+def gemm(M, N, K, dtype, out_dtype, epilogue, a, w, residual, c, ws=None, stream=None):
     _check(lib().orthrus_gemm(M, N, K, dtype, out_dtype, epilogue, _ptr(a), _ptr(w), _ptr(residual), _ptr(c),
+                              _ptr(ws), 0 if ws is None or isinstance(ws, int) else ws.numel() * ws.element_size(),
                               _stream(stream)))
 
 

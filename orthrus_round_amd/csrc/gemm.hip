@@ -1,4 +1,9 @@
 // Layer GEMMs of both views: C = epilogue(A W^T) on MFMA with fused residual add or SwiGLU.
+//
+// Decode-shaped GEMMs (M = batch x 32 rows, weights streamed from HBM once) use small output
+// tiles so that every shape has enough workgroups streaming weights; inside a workgroup the four
+// wavefronts split the k-steps four ways and sum their partial tiles in a fixed order, so results
+// are deterministic and a row's bits do not depend on the batch size.
 #include "gemm_core.hpp"
 
 namespace orthrus {
@@ -8,55 +13,80 @@ template <typename T, typename OutT, typename Cfg, int EPI>
 __global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, const T* __restrict__ W,
                                                    const OutT* residual, OutT* C, int M, int N, int K) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  T* lds = reinterpret_cast<T*>(smem);
   const int mtiles = (M + Cfg::BM - 1) / Cfg::BM;
-  int mt, nt;
-  xcd_tile_map(blockIdx.x, gridDim.x, mtiles, mt, nt);
+  int sp, mt, nt;
+  xcd_tile_map(blockIdx.x, gridDim.x, 1, mtiles, sp, mt, nt);
   const int m0 = mt * Cfg::BM, n0 = nt * Cfg::BN;
   f32x16 acc[Cfg::TM][Cfg::TN];
-  gemm_mainloop<T, Cfg>(A, W, M, N, K, m0, n0, lds, acc);
-
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hh = lane >> 5, r = lane & 31;
-  const int wm = w / Cfg::WN, wn = w % Cfg::WN;
+  if constexpr (Cfg::KSPLIT) {
+    gemm_mainloop_ks4<T, Cfg>(A, W, M, N, K, m0, n0, smem, acc);
+  } else {
+    gemm_mainloop<T, Cfg>(A, W, M, N, K, m0, n0, 0, K, smem, acc);
+  }
+  // block (i, j) of the tile: k-split tiles sum the four wave partials from LDS, plain tiles
+  // hold it in this wave's registers (wave (wm, wn) owns blocks i in [wm*TM, ..), j in [wn*TN, ..))
+  auto block = [&](int i, int j) -> f32x16 {
+    if constexpr (Cfg::KSPLIT) return ks4_sum<Cfg>(smem, i, j);
+    else return acc[i - (w / Cfg::WN) * Cfg::TM][j - (w % Cfg::WN) * Cfg::TN];
+  };
+  auto owns = [&](int q, int i, int j) -> bool {
+    if constexpr (Cfg::KSPLIT) return q % 4 == w;
+    else return i / Cfg::TM == w / Cfg::WN && j / Cfg::TN == w % Cfg::WN;
+  };
   if constexpr (EPI == ORTHRUS_EPI_SWIGLU) {
-    // columns come in (gate 32, up 32) pairs: tile j even = gate block, j+1 = its up block
+    // columns come in (gate 32, up 32) pairs: block j even = gate, j+1 = its up block
     const int NO = N / 2;
 #pragma unroll
-    for (int i = 0; i < Cfg::TM; ++i)
+    for (int i = 0; i < Cfg::BM / 32; ++i)
 #pragma unroll
-      for (int j = 0; j < Cfg::TN; j += 2) {
-        const int ng = n0 + (wn * Cfg::TN + j) * 32;  // multiple of 64
-        const int col = ng / 2 + r;
+      for (int j = 0; j < Cfg::BN / 32; j += 2) {
+        if (!owns(i * (Cfg::BN / 64) + j / 2, i, j)) continue;
+        const int ng = n0 + j * 32;  // multiple of 64
         if (ng >= N) continue;
+        const f32x16 g = block(i, j), u = block(i, j + 1);
+        const int col = ng / 2 + r;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int m = m0 + (wm * Cfg::TM + i) * 32 + acc_row(e, hh);
+          const int m = m0 + i * 32 + acc_row(e, hh);
           if (m < M) {
-            const float g = acc[i][j][e], u = acc[i][j + 1][e];
-            const float s = g / (1.0f + expf(-g));
-            C[(size_t)m * NO + col] = from_f32<OutT>(s * u);
+            const float s = g[e] / (1.0f + expf(-g[e]));
+            C[(size_t)m * NO + col] = from_f32<OutT>(s * u[e]);
           }
         }
       }
   } else {
 #pragma unroll
-    for (int i = 0; i < Cfg::TM; ++i)
+    for (int i = 0; i < Cfg::BM / 32; ++i)
 #pragma unroll
-      for (int j = 0; j < Cfg::TN; ++j) {
-        const int n = n0 + (wn * Cfg::TN + j) * 32 + r;
+      for (int j = 0; j < Cfg::BN / 32; ++j) {
+        if (!owns(i * (Cfg::BN / 32) + j, i, j)) continue;
+        const int n = n0 + j * 32 + r;
         if (n >= N) continue;
+        const f32x16 v = block(i, j);
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int m = m0 + (wm * Cfg::TM + i) * 32 + acc_row(e, hh);
+          const int m = m0 + i * 32 + acc_row(e, hh);
           if (m < M) {
-            float v = acc[i][j][e];
-            if constexpr (EPI == ORTHRUS_EPI_RESIDUAL) v = to_f32(residual[(size_t)m * N + n]) + v;
-            C[(size_t)m * N + n] = from_f32<OutT>(v);
+            float x = v[e];
+            if constexpr (EPI == ORTHRUS_EPI_RESIDUAL) x = to_f32(residual[(size_t)m * N + n]) + x;
+            C[(size_t)m * N + n] = from_f32<OutT>(x);
           }
         }
       }
   }
 }
+
+// Two families, chosen by N alone (so an output element's k order never depends on M):
+//  * N < 16384 (QKV, O, down projections): KsCfg tiles, k-steps split four ways per workgroup;
+//  * N >= 16384 (the gate/up projection): plain GemmCfg tiles, waves split the output tile.
+// Within a family the tile height follows M only to avoid idle rows.
+template <typename T> using KsSmall = KsCfg<T, 32, 64, 6>;
+template <typename T> using KsBig = KsCfg<T, 64, 64, 4>;
+template <typename T> using PlainSmall = GemmCfg<T, 32, 128, 1, 4, 4>;
+template <typename T> using PlainMid = GemmCfg<T, 64, 128, 2, 2, 3>;
+template <typename T> using PlainBig = GemmCfg<T, 128, 128, 2, 2, 2>;
+constexpr int kWideN = 16384;
 
 template <typename T, typename OutT, typename Cfg>
 int32_t launch_cfg(int M, int N, int K, int epi, const void* a, const void* w, const void* res, void* c,
@@ -70,13 +100,18 @@ int32_t launch_cfg(int M, int N, int K, int epi, const void* a, const void* w, c
   OutT* C = reinterpret_cast<OutT*>(c);
   switch (epi) {
     case ORTHRUS_EPI_STORE:
+      allow_lds(gemm_kernel<T, OutT, Cfg, ORTHRUS_EPI_STORE>, lds);
       hipLaunchKernelGGL((gemm_kernel<T, OutT, Cfg, ORTHRUS_EPI_STORE>), grid, dim3(256), lds, st, A, Wt, R, C, M, N, K);
       break;
     case ORTHRUS_EPI_RESIDUAL:
-      hipLaunchKernelGGL((gemm_kernel<T, OutT, Cfg, ORTHRUS_EPI_RESIDUAL>), grid, dim3(256), lds, st, A, Wt, R, C, M, N, K);
+      allow_lds(gemm_kernel<T, OutT, Cfg, ORTHRUS_EPI_RESIDUAL>, lds);
+      hipLaunchKernelGGL((gemm_kernel<T, OutT, Cfg, ORTHRUS_EPI_RESIDUAL>), grid, dim3(256), lds, st, A, Wt, R, C, M,
+                         N, K);
       break;
     default:
-      hipLaunchKernelGGL((gemm_kernel<T, OutT, Cfg, ORTHRUS_EPI_SWIGLU>), grid, dim3(256), lds, st, A, Wt, R, C, M, N, K);
+      allow_lds(gemm_kernel<T, OutT, Cfg, ORTHRUS_EPI_SWIGLU>, lds);
+      hipLaunchKernelGGL((gemm_kernel<T, OutT, Cfg, ORTHRUS_EPI_SWIGLU>), grid, dim3(256), lds, st, A, Wt, R, C, M, N,
+                         K);
       break;
   }
   return check_launch("orthrus_gemm");
@@ -84,10 +119,13 @@ int32_t launch_cfg(int M, int N, int K, int epi, const void* a, const void* w, c
 
 template <typename T, typename OutT>
 int32_t launch(int M, int N, int K, int epi, const void* a, const void* w, const void* res, void* c, hipStream_t st) {
-  // Tile choice depends only on (M, N); the k order is the same for all of them.
-  if (M <= 32 && epi != ORTHRUS_EPI_SWIGLU) return launch_cfg<T, OutT, GemmCfg<T, 32, 128, 1, 4>>(M, N, K, epi, a, w, res, c, st);
-  if (M <= 64) return launch_cfg<T, OutT, GemmCfg<T, 64, 128, 2, 2>>(M, N, K, epi, a, w, res, c, st);
-  return launch_cfg<T, OutT, GemmCfg<T, 128, 128, 2, 2>>(M, N, K, epi, a, w, res, c, st);
+  if (N < kWideN) {
+    if (M <= 32) return launch_cfg<T, OutT, KsSmall<T>>(M, N, K, epi, a, w, res, c, st);
+    return launch_cfg<T, OutT, KsBig<T>>(M, N, K, epi, a, w, res, c, st);
+  }
+  if (M <= 32) return launch_cfg<T, OutT, PlainSmall<T>>(M, N, K, epi, a, w, res, c, st);
+  if (M <= 64) return launch_cfg<T, OutT, PlainMid<T>>(M, N, K, epi, a, w, res, c, st);
+  return launch_cfg<T, OutT, PlainBig<T>>(M, N, K, epi, a, w, res, c, st);
 }
 
 template <typename T>
@@ -99,23 +137,35 @@ __global__ void pack_gate_up_kernel(const T* g, const T* u, T* p, int inter, int
   for (int i = threadIdx.x; i < hidden; i += blockDim.x) dst[i] = src[i];
 }
 
-}  // namespace
-}  // namespace orthrus
-
-using namespace orthrus;
-
-extern "C" int32_t orthrus_gemm(int32_t M, int32_t N, int32_t K, int32_t dtype, int32_t out_dtype, int32_t epilogue,
-                                const void* a, const void* w, const void* residual, void* c, void* stream) {
+int32_t validate(int32_t M, int32_t N, int32_t K, int32_t dtype, int32_t out_dtype, int32_t epilogue) {
   ORTHRUS_REQUIRE(M >= 0 && N > 0 && K > 0, ORTHRUS_ERR_INVALID_ARG, "gemm: bad sizes M=%d N=%d K=%d", M, N, K);
   ORTHRUS_REQUIRE(K % 64 == 0, ORTHRUS_ERR_UNSUPPORTED, "gemm: K=%d not a multiple of 64", K);
   ORTHRUS_REQUIRE(valid_dtype(dtype) && valid_dtype(out_dtype), ORTHRUS_ERR_INVALID_ARG, "gemm: bad dtype");
   ORTHRUS_REQUIRE(epilogue >= 0 && epilogue <= 2, ORTHRUS_ERR_INVALID_ARG, "gemm: bad epilogue %d", epilogue);
   ORTHRUS_REQUIRE(epilogue != ORTHRUS_EPI_SWIGLU || N % 64 == 0, ORTHRUS_ERR_INVALID_ARG,
                   "gemm: SwiGLU needs N %% 64 == 0 (got %d)", N);
-  ORTHRUS_REQUIRE(a && w && c, ORTHRUS_ERR_INVALID_ARG, "gemm: null pointer");
-  ORTHRUS_REQUIRE(epilogue != ORTHRUS_EPI_RESIDUAL || residual, ORTHRUS_ERR_INVALID_ARG, "gemm: residual is null");
   ORTHRUS_REQUIRE(!(dtype == ORTHRUS_F32 && out_dtype == ORTHRUS_BF16), ORTHRUS_ERR_UNSUPPORTED,
                   "gemm: fp32 inputs with bf16 output not built");
+  return ORTHRUS_OK;
+}
+
+}  // namespace
+}  // namespace orthrus
+
+using namespace orthrus;
+
+extern "C" size_t orthrus_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t dtype, int32_t epilogue) {
+  (void)M; (void)N; (void)K; (void)dtype; (void)epilogue;
+  return 0;
+}
+
+extern "C" int32_t orthrus_gemm(int32_t M, int32_t N, int32_t K, int32_t dtype, int32_t out_dtype, int32_t epilogue,
+                                const void* a, const void* w, const void* residual, void* c, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  (void)workspace; (void)workspace_bytes;
+  if (int32_t s = validate(M, N, K, dtype, out_dtype, epilogue)) return s;
+  ORTHRUS_REQUIRE(a && w && c, ORTHRUS_ERR_INVALID_ARG, "gemm: null pointer");
+  ORTHRUS_REQUIRE(epilogue != ORTHRUS_EPI_RESIDUAL || residual, ORTHRUS_ERR_INVALID_ARG, "gemm: residual is null");
   if (M == 0) return ORTHRUS_OK;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (dtype == ORTHRUS_BF16) {

@@ -34,13 +34,13 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
 template <typename T, typename Cfg>
 __global__ __launch_bounds__(256) void lmhead_kernel(LmArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  T* lds = reinterpret_cast<T*>(smem);
   const int mtiles = (a.M + Cfg::BM - 1) / Cfg::BM;
-  int mt, nt;
-  xcd_tile_map(blockIdx.x, gridDim.x, mtiles, mt, nt);
+  int sp, mt, nt;
+  xcd_tile_map(blockIdx.x, gridDim.x, 1, mtiles, sp, mt, nt);
   const int m0 = mt * Cfg::BM, n0 = nt * Cfg::BN;
   f32x16 acc[Cfg::TM][Cfg::TN];
-  gemm_mainloop<T, Cfg>(reinterpret_cast<const T*>(a.h), reinterpret_cast<const T*>(a.w), a.M, a.N, a.K, m0, n0, lds, acc);
+  gemm_mainloop<T, Cfg>(reinterpret_cast<const T*>(a.h), reinterpret_cast<const T*>(a.w), a.M, a.N, a.K, m0, n0, 0, a.K,
+                        smem, acc);
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hh = lane >> 5, r = lane & 31;
   const int wm = w / Cfg::WN, wn = w % Cfg::WN;
@@ -148,6 +148,7 @@ template <typename T, typename Cfg>
 int32_t launch(LmArgs& a, hipStream_t st) {
   const int mtiles = (a.M + Cfg::BM - 1) / Cfg::BM;
   const size_t lds = std::max(Cfg::LDS_BYTES, (size_t)Cfg::BM * Cfg::WN * 16);
+  allow_lds(lmhead_kernel<T, Cfg>, lds);
   hipLaunchKernelGGL((lmhead_kernel<T, Cfg>), dim3(mtiles * a.ntiles), dim3(256), lds, st, a);
   return check_launch("orthrus_lmhead_argmax");
 }
@@ -195,13 +196,13 @@ extern "C" int32_t orthrus_lmhead_argmax(const orthrus_lmhead_desc_t* d, const v
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   int32_t s;
   if (d->dtype == ORTHRUS_BF16) {
-    if (a.M <= 32) s = launch<bf16, GemmCfg<bf16, 32, kLmBN, 1, 4>>(a, st);
-    else if (a.M <= 64) s = launch<bf16, GemmCfg<bf16, 64, kLmBN, 2, 2>>(a, st);
-    else s = launch<bf16, GemmCfg<bf16, 128, kLmBN, 2, 2>>(a, st);
+    if (a.M <= 32) s = launch<bf16, GemmCfg<bf16, 32, kLmBN, 1, 4, 4>>(a, st);
+    else if (a.M <= 64) s = launch<bf16, GemmCfg<bf16, 64, kLmBN, 2, 2, 3>>(a, st);
+    else s = launch<bf16, GemmCfg<bf16, 128, kLmBN, 2, 2, 2>>(a, st);
   } else {
-    if (a.M <= 32) s = launch<float, GemmCfg<float, 32, kLmBN, 1, 4>>(a, st);
-    else if (a.M <= 64) s = launch<float, GemmCfg<float, 64, kLmBN, 2, 2>>(a, st);
-    else s = launch<float, GemmCfg<float, 128, kLmBN, 2, 2>>(a, st);
+    if (a.M <= 32) s = launch<float, GemmCfg<float, 32, kLmBN, 1, 4, 4>>(a, st);
+    else if (a.M <= 64) s = launch<float, GemmCfg<float, 64, kLmBN, 2, 2, 3>>(a, st);
+    else s = launch<float, GemmCfg<float, 128, kLmBN, 2, 2, 2>>(a, st);
   }
   if (s != ORTHRUS_OK) return s;
   hipLaunchKernelGGL(lmhead_finalize, dim3(a.M), dim3(64), 0, st, a.part_best, a.part_m, a.part_s, a.ntiles, token_out,

@@ -114,6 +114,11 @@ class Decoder:
         self.k_blk = torch.empty((self.B, block, Hkv, D), dtype=self.tdt, device=self.dev)
         self.v_blk = torch.empty_like(self.k_blk)
         self.attn_ws = {}
+        gw = 0
+        for (n, k, e) in ((self.nqkv, H, L.EPI_STORE), (H, Hq * D, L.EPI_RESIDUAL), (2 * I, H, L.EPI_SWIGLU),
+                          (H, I, L.EPI_RESIDUAL)):
+            gw = max(gw, L.gemm_workspace_bytes(M, n, k, self.dt, e))
+        self.gemm_ws = torch.zeros(max(gw, 256), dtype=torch.uint8, device=self.dev)  # counters start at zero
         self.lm_ws = torch.empty(L.lmhead_workspace_bytes(L.lmhead_desc(M, H, V, self.dt)), dtype=torch.uint8,
                                  device=self.dev)
         # round state
@@ -151,7 +156,7 @@ class Decoder:
         x, a = self.x[:M], self.a[:M]
         for l, Wl in enumerate(self.layers):
             L.rmsnorm(M, H, dt, x, Wl["attn_norm"], s.eps, a)
-            L.gemm(M, self.nqkv, H, dt, dt, L.EPI_STORE, a, Wl["qkv_" + view], None, self.qkv)
+            L.gemm(M, self.nqkv, H, dt, dt, L.EPI_STORE, a, Wl["qkv_" + view], None, self.qkv, self.gemm_ws)
             if draft:
                 L.rope_kv_write(nb, kb, Hq, Hkv, D, self.page, self.max_pages, dt, self.qkv, self.rope,
                                 self.max_pos, ctx, None, self.q, self.k_blk, self.v_blk)
@@ -161,10 +166,10 @@ class Decoder:
                 L.rope_kv_write(nb, kb, Hq, Hkv, D, self.page, self.max_pages, dt, self.qkv, self.rope,
                                 self.max_pos, ctx, self.page_table, self.q, self.k_pages[l], self.v_pages[l])
                 L.verify_attn(desc, self.q, self.k_pages[l], self.v_pages[l], self.page_table, ctx, self.o, ws)
-            L.gemm(M, H, Hq * D, dt, dt, L.EPI_RESIDUAL, self.o, Wl["o_" + view], x, x)
+            L.gemm(M, H, Hq * D, dt, dt, L.EPI_RESIDUAL, self.o, Wl["o_" + view], x, x, self.gemm_ws)
             L.rmsnorm(M, H, dt, x, Wl["mlp_norm"], s.eps, a)
-            L.gemm(M, 2 * I, H, dt, dt, L.EPI_SWIGLU, a, Wl["gate_up"], None, self.h)
-            L.gemm(M, H, I, dt, dt, L.EPI_RESIDUAL, self.h, Wl["down"], x, x)
+            L.gemm(M, 2 * I, H, dt, dt, L.EPI_SWIGLU, a, Wl["gate_up"], None, self.h, self.gemm_ws)
+            L.gemm(M, H, I, dt, dt, L.EPI_RESIDUAL, self.h, Wl["down"], x, x, self.gemm_ws)
 
     def _lm_head(self, nb, kb, tokens, temperature=0.0, seed=0, stream_id=L.STREAM_DRAFT, logits=None, lse=None):
         s = self.shape

@@ -66,3 +66,8 @@ def test_attention_descriptor_validation():
     for d in bad:
         with pytest.raises(ora.OrthrusError):
             ora.verify_attn(d, 1, 1, 1, 1, 1, 1, None, stream=0)
+
+
+def test_gemm_needs_no_workspace():
+    assert ora.gemm_workspace_bytes(256, 4096, 4096, ora.BF16, ora.EPI_STORE) == 0
+    assert ora.gemm_workspace_bytes(8, 24576, 4096, ora.BF16, ora.EPI_SWIGLU) == 0

@@ -26,6 +26,10 @@ def dev(x, dtype=None):
     return t.to(DEV)
 
 
+def gemm_ws(M, N, K, dtype, epi):
+    return torch.zeros(max(256, ora.gemm_workspace_bytes(M, N, K, dtype, epi)), dtype=torch.uint8, device=DEV)
+
+
 def tie_ok(z, gpu_id, ref_id):
     """Same id, or an oracle near-tie between the two ids."""
     if gpu_id == ref_id:
@@ -263,7 +267,8 @@ def test_philox_words_match_numpy():
 # ------------------------------------------------------------------- support kernels
 
 @pytest.mark.parametrize("dtype", [ora.BF16, ora.F32])
-@pytest.mark.parametrize("M,N,K", [(256, 6144, 4096), (8, 4096, 4096), (45, 1024, 256), (100, 320, 128)])
+@pytest.mark.parametrize("M,N,K", [(256, 6144, 4096), (8, 4096, 4096), (45, 1024, 256), (100, 320, 128),
+                                   (256, 16384, 256), (40, 16448, 128)])
 @pytest.mark.parametrize("epi", [ora.EPI_STORE, ora.EPI_RESIDUAL, ora.EPI_SWIGLU])
 def test_gemm_epilogues(dtype, M, N, K, epi):
     if epi == ora.EPI_SWIGLU and N % 64:
@@ -277,7 +282,7 @@ def test_gemm_epilogues(dtype, M, N, K, epi):
         g = torch.empty((M, ncol), dtype=torch.bfloat16 if bf else torch.float32, device=DEV)
         packed = torch.empty((N, K), dtype=g.dtype, device=DEV)
         ora.pack_gate_up(ncol, K, dtype, dev(w[:ncol], dtype), dev(w[ncol:], dtype), packed)
-        ora.gemm(M, N, K, dtype, dtype, epi, dev(a, dtype), packed, None, g)
+        ora.gemm(M, N, K, dtype, dtype, epi, dev(a, dtype), packed, None, g, gemm_ws(M, N, K, dtype, epi))
         gg, uu = z[:, :ncol], z[:, ncol:]
         ref = gg / (1 + np.exp(-gg)) * uu
     else:
@@ -285,7 +290,8 @@ def test_gemm_epilogues(dtype, M, N, K, epi):
         r_t = dev(res, dtype) if res is not None else None
         if r_t is not None:
             c.copy_(r_t)  # in place: c aliases the residual
-        ora.gemm(M, N, K, dtype, dtype, epi, dev(a, dtype), dev(w, dtype), c if r_t is not None else None, c)
+        ora.gemm(M, N, K, dtype, dtype, epi, dev(a, dtype), dev(w, dtype), c if r_t is not None else None, c,
+                 gemm_ws(M, N, K, dtype, epi))
         g = c
         ref = z + (res.astype(np.float64) if res is not None else 0)
     torch.cuda.synchronize()
@@ -295,12 +301,14 @@ def test_gemm_epilogues(dtype, M, N, K, epi):
 
 
 @pytest.mark.parametrize("dtype", [ora.BF16, ora.F32])
-def test_gemm_row_invariance(dtype):
-    a, w = synth.lmhead_inputs(22, 256, 4096, 1024, bf16=(dtype == ora.BF16))
+@pytest.mark.parametrize("N", [1024, 16384])
+def test_gemm_row_invariance(dtype, N):
+    a, w = synth.lmhead_inputs(22, 256, 4096, N, bf16=(dtype == ora.BF16))
     outs = []
     for m in (256, 64, 32, 1):
-        c = torch.empty((m, 1024), dtype=torch.float32, device=DEV)
-        ora.gemm(m, 1024, 4096, dtype, ora.F32, ora.EPI_STORE, dev(a[:m], dtype), dev(w, dtype), None, c)
+        c = torch.empty((m, N), dtype=torch.float32, device=DEV)
+        ora.gemm(m, N, 4096, dtype, ora.F32, ora.EPI_STORE, dev(a[:m], dtype), dev(w, dtype), None, c,
+                 gemm_ws(m, N, 4096, dtype, ora.EPI_STORE))
         outs.append(c.cpu().numpy())
     for o in outs[1:]:
         assert np.array_equal(o, outs[0][: o.shape[0]])
@@ -377,3 +385,17 @@ def test_embed_block_modes():
     ora.embed_block(2, 2, H, ora.F32, Et, None, dev(toks), 4, 1, V - 1, x[:4])    # prefill chunk
     ref = np.stack([E[2], E[3], E[8], E[7]])
     assert np.array_equal(x[:4].cpu().numpy(), ref)
+
+
+def test_gemm_is_repeatable_and_large_k_accurate():
+    """Deterministic: three calls give the same bits (no cross-workgroup reduction order)."""
+    M, N, K = 256, 4096, 12288
+    a, w = synth.lmhead_inputs(26, M, K, N)
+    outs = []
+    for _ in range(3):
+        c = torch.empty((M, N), dtype=torch.float32, device=DEV)
+        ora.gemm(M, N, K, ora.BF16, ora.F32, ora.EPI_STORE, dev(a, ora.BF16), dev(w, ora.BF16), None, c)
+        outs.append(c.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
+    ref = a[:16].astype(np.float64) @ w.astype(np.float64).T
+    assert np.abs(outs[0][:16] - ref).max() <= 1e-5 * np.abs(ref).max()
