@@ -95,15 +95,44 @@ def kernel_table(dec, ctx_np):
     return tab
 
 
+def source_digest():
+    """sha256 over the kernel sources (orthrus_round_amd/csrc/*, sorted by name)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for p in sorted(glob.glob(os.path.join(root, "orthrus_round_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(name):
+    """HBM bytes per launch of a kernel from the committed FETCH_SIZE/WRITE_SIZE profile
+    (profiles/traffic.json, counts scaled by a plain 256 MiB copy), or None when the kernel
+    sources changed after the counters were taken."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            prof = json.load(f)
+    except OSError:
+        return None
+    if prof.get("source_sha256") != source_digest():
+        return None
+    rec = prof.get("bench_kernels", {}).get(name)
+    return None if rec is None else rec["bytes"]
+
+
 def roofline_of(name, rec, bound="hbm"):
+    traffic = profiled_traffic(name)
     if bound == "hbm":
         ach = rec["bytes"] / (rec["ms"] * 1e-3) / 1e9
         return {"kernel": name, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_launch": rec["bytes"],
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic, "bytes_per_launch": rec["bytes"],
                 "ms_per_launch": round(rec["ms"], 5)}
     ach = rec["flops"] / (rec["ms"] * 1e-3) / 1e12
     return {"kernel": name, "bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None, "flops_per_launch": rec["flops"],
+            "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": traffic, "flops_per_launch": rec["flops"],
             "ms_per_launch": round(rec["ms"], 5)}
 
 
@@ -250,6 +279,12 @@ def main():
     ar_ms = (time.perf_counter() - ta) / 20 * 1e3
 
     attn = None if args.no_attn else attention_roofline(args.kv_chunk)
+    # calibration for HBM-traffic counters: one plain 256 MiB device copy
+    cal_src = torch.ones(256 * 2**20, dtype=torch.uint8, device="cuda")
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    torch.cuda.synchronize()
+    del cal_src, cal_dst
     tokens_per_round_seq = committed / (args.steps * args.batch)
     cpu = None
     if not args.no_cpu_baseline:

@@ -78,7 +78,7 @@ const char* orthrus_last_error(void);
 typedef struct {
   int32_t batch;
   int32_t q_heads;
-  int32_t kv_heads;   /* q_heads % kv_heads == 0, group in {1, 2, 4, 8}            */
+  int32_t kv_heads;   /* q_heads % kv_heads == 0, group q_heads/kv_heads in {2, 4} */
   int32_t head_dim;   /* 64 or 128                                                  */
   int32_t block;      /* rows per sequence, 1..32                                   */
   int32_t page_size;  /* keys per page, a divisor of 32 or a multiple of 32         */
@@ -188,10 +188,12 @@ typedef enum {
 } orthrus_epilogue_t;
 
 /* c [M, N'] = epilogue(a [M, K] . w [N, K]^T), fp32 accumulation.  K % 64 == 0; SwiGLU needs
- * N % 64 == 0.  The k-steps of every output tile are split four ways inside one workgroup and
- * the four partial sums are added in a fixed order, so an output element's bits never depend
- * on M (a row computed alone equals the same row inside a larger batch).  The workspace
- * arguments are reserved: orthrus_gemm_workspace_bytes() returns 0 and NULL/0 may be passed. */
+ * N % 64 == 0.  The summation order of an output element depends on (N, K) only: for
+ * N < 16384 the k-steps of a tile are dealt four ways inside one workgroup and the four
+ * partial sums are added in a fixed order; for wider N each wave runs the k loop in order.
+ * So a row computed alone has the same bits as the same row inside a larger batch.  The
+ * workspace arguments are reserved: orthrus_gemm_workspace_bytes() returns 0 and NULL/0 may
+ * be passed. */
 size_t orthrus_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t dtype,
                                     int32_t epilogue);
 int32_t orthrus_gemm(int32_t M, int32_t N, int32_t K, int32_t dtype, int32_t out_dtype,

@@ -83,6 +83,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, cons
 // Within a family the tile height follows M only to avoid idle rows.
 template <typename T> using KsSmall = KsCfg<T, 32, 64, 6>;
 template <typename T> using KsBig = KsCfg<T, 64, 64, 4>;
+template <typename T> using KsBigDeep = KsCfg<T, 64, 64, 6>;  // long reductions (K > 8192)
 template <typename T> using PlainSmall = GemmCfg<T, 32, 128, 1, 4, 4>;
 template <typename T> using PlainMid = GemmCfg<T, 64, 128, 2, 2, 3>;
 template <typename T> using PlainBig = GemmCfg<T, 128, 128, 2, 2, 2>;
@@ -121,6 +122,7 @@ template <typename T, typename OutT>
 int32_t launch(int M, int N, int K, int epi, const void* a, const void* w, const void* res, void* c, hipStream_t st) {
   if (N < kWideN) {
     if (M <= 32) return launch_cfg<T, OutT, KsSmall<T>>(M, N, K, epi, a, w, res, c, st);
+    if (K > 8192) return launch_cfg<T, OutT, KsBigDeep<T>>(M, N, K, epi, a, w, res, c, st);
     return launch_cfg<T, OutT, KsBig<T>>(M, N, K, epi, a, w, res, c, st);
   }
   if (M <= 32) return launch_cfg<T, OutT, PlainSmall<T>>(M, N, K, epi, a, w, res, c, st);

@@ -39,9 +39,15 @@ struct GemmCfg {
 // Map the linear workgroup id to (split, m_tile, n_tile) so that the splits and m-tiles sharing
 // a slice of W run back to back on the same XCD (workgroups are dealt round-robin to the 8 XCDs,
 // each with its own L2): W then comes from HBM once and split partials stay in that L2.
+// XCD x receives ids x, x+8, ...; with total = 8q + r the first r XCDs get q+1 of them, and XCD x
+// takes the contiguous logical range starting at x*q + min(x, r), so the map is a bijection.
+__device__ __forceinline__ int xcd_linear(int id, int total) {
+  const int x = id & 7, slot = id >> 3, q = total >> 3, r = total & 7;
+  return x * q + (x < r ? x : r) + slot;
+}
+
 __device__ __forceinline__ void xcd_tile_map(int id, int total, int splits, int mtiles, int& s, int& mt, int& nt) {
-  int L = id;
-  if (total % 8 == 0) L = (id % 8) * (total / 8) + id / 8;
+  int L = xcd_linear(id, total);
   s = L % splits;
   L /= splits;
   mt = L % mtiles;
