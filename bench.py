@@ -36,17 +36,34 @@ def parse():
     return p.parse_args()
 
 
-def event_time_ms(fn, iters=10):
+_FLUSH = None
+
+
+def flush_caches():
+    """Evict L2 and the 256 MiB infinity cache by READING 512 MiB (a write would leave dirty
+    lines whose write-back would then compete with the next timed kernel)."""
+    global _FLUSH
+    import torch
+    if _FLUSH is None:
+        _FLUSH = torch.zeros(128 * 2**20, dtype=torch.float32, device="cuda")
+    _FLUSH.sum()
+
+
+def event_time_ms(fn, iters=12):
+    """Median duration of one launch of `fn`, cold (caches flushed before each launch), timed with
+    HIP events on the current stream, the stream the library launches on."""
     import torch
     fn()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    s.record()
+    times = []
     for _ in range(iters):
+        flush_caches()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
         fn()
-    e.record()
-    torch.cuda.synchronize()
-    return s.elapsed_time(e) / iters
+        e.record()
+        torch.cuda.synchronize()
+        times.append(s.elapsed_time(e))
+    return float(np.median(times[2:]))
 
 
 def kernel_table(dec, ctx_np):
@@ -153,7 +170,6 @@ def attention_roofline(kv_chunk):
     pt, cl = dv(inp.page_table, False), dv(inp.ctx, False)
     kb, vb = dv(inp.k_blk), dv(inp.v_blk)
     out = torch.empty((16, 32, 32, 128), dtype=torch.float32, device="cuda")
-    flush = torch.empty(512 * 2**20, dtype=torch.uint8, device="cuda")
     res = {}
     n_sum = int(ctx.sum())
     for name, fn, keys in [
@@ -161,20 +177,11 @@ def attention_roofline(kv_chunk):
         ("verify", lambda: ora.verify_attn(desc, q, pk, pv, pt, cl, out, ws), n_sum + 16 * 32),
     ]:
         byts = keys * 8 * 128 * 2 * 2 + q.numel() * 2 + out.numel() * 4
-        fn()
-        times = []
-        for _ in range(20):
-            flush.fill_(1)  # evict L2 and MALL (512 MiB > 256 MiB infinity cache)
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s.record()
-            fn()
-            e.record()
-            torch.cuda.synchronize()
-            times.append(s.elapsed_time(e))
-        ms = float(np.median(times))
+        ms = event_time_ms(fn, 20)
         res[name] = {"ms": round(ms, 5), "bytes": byts, "GBs": round(byts / ms / 1e6, 1),
                      "frac": round(byts / ms / 1e6 / HBM_PEAK_GBS, 4)}
-    return {"workload": "batch 16, 32Q/8KV, D128, ctx U[512,16384], 16-token paged random order, bf16->fp32, cold",
+    return {"workload": "batch 16, 32Q/8KV, D128, ctx U[512,16384], 16-token paged random order, bf16->fp32, "
+                        "cold (512 MiB read before each launch)",
             "sum_ctx": n_sum, **res}
 
 

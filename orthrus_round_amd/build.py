@@ -19,6 +19,9 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
 ]
+# Per-source flags.  attn.hip keeps its MFMA accumulators in ordinary VGPRs: the online-softmax
+# rescale works on them with vector ALU instructions, which cannot address accumulation registers.
+EXTRA = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def build(verbose: bool = False, jobs: int = 6) -> str:
@@ -26,7 +29,8 @@ def build(verbose: bool = False, jobs: int = 6) -> str:
 
     def compile_one(src):
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-I", os.path.join(ROOT, "include"), "-c",
+               os.path.join(CSRC, src), "-o", obj]
         p = subprocess.run(cmd, capture_output=True, text=True)
         if p.returncode != 0:
             raise RuntimeError(f"hipcc failed for {src}:\n{p.stderr[-6000:]}")

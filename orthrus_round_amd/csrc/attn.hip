@@ -9,11 +9,12 @@
 //  * the G query heads that share a kv head are G wavefronts; each wavefront owns one query
 //    head's 32 block rows, so one K/V tile staged in LDS serves G*32 query rows (GQA reuse);
 //  * keys are streamed in 32-key tiles at absolute positions 32t..32t+31, gathered from the
-//    paged cache with direct 16-byte global->LDS loads into a ring of 4 tile stages (3 in
-//    flight while one is used); K rows are chunk-swizzled against bank conflicts, V rows are
-//    read in place;
+//    paged cache with direct 16-byte global->LDS loads into a ring of S tile stages (S-1 tiles
+//    in flight while one is used); K and V rows are chunk-swizzled against bank conflicts, and
+//    the loop is unrolled by S so every LDS address is a register plus an immediate;
 //  * S^T = K Q^T and O^T += V^T P^T run on 32x32 MFMA (bf16 x16 or fp32 x2), so a lane owns one
-//    query row of S and O and the online-softmax rescale is lane-local; in bf16 the
+//    query row of S and O and the online-softmax bookkeeping is lane-local; the reference
+//    maximum is raised lazily (only when a tile exceeds it by 2^8), per row; in bf16 the
 //    probabilities enter the PV product as a hi + lo pair of bf16 terms;
 //  * fixed chunks of kv_chunk keys: a sequence with one chunk writes its output directly,
 //    longer ones write (m, l, acc) partials that a combine kernel merges in chunk order.
@@ -40,7 +41,7 @@ struct AttnArgs {
   void* out;
   float* part_acc;
   float* part_ml;
-  int32_t Hq, Hkv, K, page, max_pages, max_ctx, chunk, nchunk_max;
+  int32_t Hq, Hkv, K, page, page_shift, max_pages, max_ctx, chunk, nchunk_max;
   float scale_log2;
 };
 
@@ -61,68 +62,89 @@ __device__ __forceinline__ uint32_t lds_offset(const unsigned char* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)p;
 }
 
-// Eight gfx950 transposed LDS reads (ds_read_b64_tr_b16: 64 bits per lane, transposed within
-// groups of 16 lanes) and the wait for them, in one asm block: the compiler cannot pair the
-// builtin with the direct global->LDS tile loads and would drain every load in flight first.
-// Outputs are early-clobber: a read may land before a later read has consumed its address.
-__device__ __forceinline__ void read_tr16_x8(const uint32_t (&addr)[8], u32x2 (&out)[8]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %8\n"
-      "ds_read_b64_tr_b16 %1, %9\n"
-      "ds_read_b64_tr_b16 %2, %10\n"
-      "ds_read_b64_tr_b16 %3, %11\n"
-      "ds_read_b64_tr_b16 %4, %12\n"
-      "ds_read_b64_tr_b16 %5, %13\n"
-      "ds_read_b64_tr_b16 %6, %14\n"
-      "ds_read_b64_tr_b16 %7, %15\n"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3]), "=&v"(out[4]), "=&v"(out[5]), "=&v"(out[6]),
-        "=&v"(out[7])
-      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "v"(addr[4]), "v"(addr[5]), "v"(addr[6]),
-        "v"(addr[7])
-      : "memory");
-}
-
 template <int N> __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+
+template <int I> struct Int { static constexpr int value = I; };
+template <int N, int I = 0, typename F> __device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(Int<I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+// Eight gfx950 transposed LDS reads (ds_read_b64_tr_b16: 64 bits per lane, transposed within
+// groups of 16 lanes) and the wait for them, in one asm block: the compiler cannot pair the
+// builtin with the direct global->LDS tile loads and would drain every load in flight first.
+// Outputs are early-clobber: a read may land before a later read has consumed its address.
+// OFF is a compile-time byte offset added to every address (the instruction's immediate).
+template <int OFF>
+__device__ __forceinline__ void read_tr16_x8_at(const uint32_t (&addr)[8], u32x2 (&out)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:%16\n"
+      "ds_read_b64_tr_b16 %1, %9 offset:%16\n"
+      "ds_read_b64_tr_b16 %2, %10 offset:%16\n"
+      "ds_read_b64_tr_b16 %3, %11 offset:%16\n"
+      "ds_read_b64_tr_b16 %4, %12 offset:%16\n"
+      "ds_read_b64_tr_b16 %5, %13 offset:%16\n"
+      "ds_read_b64_tr_b16 %6, %14 offset:%16\n"
+      "ds_read_b64_tr_b16 %7, %15 offset:%16\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3]), "=&v"(out[4]), "=&v"(out[5]), "=&v"(out[6]),
+        "=&v"(out[7])
+      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "v"(addr[4]), "v"(addr[5]), "v"(addr[6]),
+        "v"(addr[7]), "n"(OFF)
+      : "memory");
+}
+
+#ifndef ORTHRUS_ATTN_STAGES
+#define ORTHRUS_ATTN_STAGES 3
+#endif
 
 template <typename T, int D, int G>
 struct AttnTile {
   static constexpr int NT = 64 * G;
   static constexpr int CPR = D * (int)sizeof(T) / 16;         // 16-byte chunks per key row
   static constexpr int ROWB = CPR * 16;
-  static constexpr int NI_ = 32 * CPR / NT;
+  static constexpr int RPL = 64 / CPR;                         // key rows per wave load
   static constexpr int TILE_BYTES = 32 * ROWB;                 // one 32-key tile of K (or V)
   static constexpr int STAGE_BYTES = 2 * TILE_BYTES;           // K tile then V tile
-#ifndef ORTHRUS_ATTN_STAGES
-#define ORTHRUS_ATTN_STAGES 4
-#endif
   static constexpr int NI = 32 * CPR / NT;                     // wave loads per thread per tile (K or V)
-  // ring depth, capped so the loads allowed in flight fit the 6-bit vmcnt
+  // ring depth: loads allowed in flight must fit the 6-bit vmcnt, stage offsets the 16-bit
+  // LDS immediate, and the ring the 160 KiB of LDS
   static constexpr int S_VM = 2 + 63 / (2 * NI);
-  static constexpr int S_LDS = (160 * 1024 - 2048) / (2 * 32 * ROWB);
-  static constexpr int STAGES = ORTHRUS_ATTN_STAGES < S_VM ? (ORTHRUS_ATTN_STAGES < S_LDS ? ORTHRUS_ATTN_STAGES : S_LDS)
-                                                           : (S_VM < S_LDS ? S_VM : S_LDS);
+  static constexpr int S_IMM = sizeof(T) == 2 ? (65535 - TILE_BYTES - 16 * ROWB) / STAGE_BYTES + 1 : 64;
+  static constexpr int S_LDS = (160 * 1024 - 2048) / STAGE_BYTES;
+  static constexpr int S_CAP = S_VM < S_IMM ? (S_VM < S_LDS ? S_VM : S_LDS) : (S_IMM < S_LDS ? S_IMM : S_LDS);
+  static constexpr int STAGES = ORTHRUS_ATTN_STAGES < S_CAP ? ORTHRUS_ATTN_STAGES : S_CAP;
+  static_assert(STAGES >= 2, "ring needs two stages");
   static_assert(NI >= 1 && NI * NT == 32 * CPR, "tile must split evenly over the workgroup");
   static constexpr size_t LDS_BYTES = (size_t)STAGES * STAGE_BYTES;
-  // K rows are stored with their 16-byte chunks XOR-swizzled so that 32 lanes reading the same
-  // chunk of 32 different rows hit distinct LDS banks.
-  __device__ __forceinline__ static int swz(int row) { return CPR >= 16 ? (row & 15) : ((row >> 1) & 7); }
+  // K and V rows are stored with their 16-byte chunks XOR-swizzled so that 32 lanes reading the
+  // same chunk of 32 different rows hit distinct LDS banks.
+  __host__ __device__ static constexpr int swz(int row) { return CPR >= 16 ? (row & 15) : ((row >> 1) & 7); }
 };
+
+// Softmax bookkeeping is in log2 units.  A row's reference maximum m is only raised when a tile
+// brings a score more than kLazy above it; otherwise exp2(s - m) <= 2^kLazy and the running sums
+// keep their old reference, which is exact because numerator and denominator share it.  The
+// decision is per row, so a row's bits never depend on the other rows of the wavefront.
+constexpr float kLazy = 8.0f;
 
 template <typename T, typename OutT, int D, int G, bool DRAFT>
 __global__ __launch_bounds__(64 * G) void attn_kernel(AttnArgs a) {
   using MF = Mfma<T>;
   using TL = AttnTile<T, D, G>;
-  constexpr int NT = TL::NT, CPR = TL::CPR, ROWB = TL::ROWB, NI = TL::NI, S = TL::STAGES;
+  constexpr int NT = TL::NT, CPR = TL::CPR, ROWB = TL::ROWB, NI = TL::NI, S = TL::STAGES, RPL = TL::RPL;
   constexpr int EPC = 16 / sizeof(T);
   constexpr int KSTEP = MF::KSTEP, KW = MF::KW;
   constexpr int NKK = D / KSTEP;
   constexpr int NDB = D / 32;
   constexpr bool BF = std::is_same<T, bf16>::value;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  __shared__ int page_lds[kMaxChunkPages];
 
   const int b = blockIdx.z, hk = blockIdx.y, c = blockIdx.x;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, hh = lane >> 5, r = lane & 31;
@@ -166,79 +188,101 @@ __global__ __launch_bounds__(64 * G) void attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < NDB; ++i) o[i] = f32x16{};
   float m_run = kNegInf, l_run = 0.0f;
+  const float csc = a.scale_log2;
 
-  const T* kpages = reinterpret_cast<const T*>(a.kp);
-  const T* vpages = reinterpret_cast<const T*>(a.vp);
-  const int32_t* ptab = a.page_table + (size_t)b * a.max_pages;
-
-  // Tile t -> LDS stage buf with direct 16-byte global->LDS loads.  Wave load j of wave w covers
-  // the tile's chunks [(j*G + w)*64, +64): rows row0 .. row0 + 64/CPR - 1, slot idx%CPR.  Rows past
-  // the chunk's last key read a clamped valid key: their scores are masked to -inf, so they weigh
-  // exactly 0.  The rows of one wave load share a page (page_size % (64/CPR) == 0, checked on the
-  // host), so its physical page comes from one scalar page-table read.  Past the last tile the
-  // same loads re-read the last tile (an L2 hit) so that every iteration has the same number of
-  // loads in flight and the loop body stays branch-free.
-  constexpr int RPL = 64 / CPR;  // key rows per wave load
   // the chunk's physical pages, read once into LDS (keeps page lookups off the vector-memory
   // counter that tracks the tile loads in flight)
-  __shared__ int page_lds[kMaxChunkPages];
   {
-    const int first = kbeg / a.page;
-    const int np = kend > kbeg ? (kend - 1) / a.page - first + 1 : 0;
-    for (int i = tid; i < np; i += NT) page_lds[i] = ptab[first + i];
+    const int first = kbeg >> a.page_shift;
+    const int np = kend > kbeg ? ((kend - 1) >> a.page_shift) - first + 1 : 0;
+    for (int i = tid; i < np; i += NT) page_lds[i] = a.page_table[(size_t)b * a.max_pages + first + i];
     __syncthreads();
   }
-  const size_t head_stride = (size_t)a.page * D;                        // elements
-  const size_t page_stride = (size_t)a.Hkv * head_stride;
-  const T* kblk = reinterpret_cast<const T*>(a.kb) + (size_t)b * K * a.Hkv * D + (size_t)hk * D;
-  const T* vblk = reinterpret_cast<const T*>(a.vb) + (size_t)b * K * a.Hkv * D + (size_t)hk * D;
-  auto issue = [&](int t, int buf) {
+
+  // Tile loads.  Wave load j of wave w fills LDS bytes [(j*G + w)*1024, +1024) of the tile: key
+  // rows row0 = (j*G + w)*RPL .. row0 + RPL - 1, lane -> (row0 + lane / CPR, 16-byte slot
+  // lane % CPR), whose global chunk is slot ^ swz(row).  The RPL rows of one wave load share a
+  // page (page_size % RPL == 0, checked on the host), so its page id is one wave-uniform LDS read.
+  // Rows past the chunk's last key (only in its last tile) re-read that key: their scores are
+  // masked to -inf and weigh exactly 0.  Past the last tile the same loads re-read the last tile
+  // (an L2 hit), so every iteration keeps the same number of loads in flight.
+  const size_t head_stride_b = (size_t)a.page * D * sizeof(T);
+  const size_t page_stride_b = (size_t)a.Hkv * head_stride_b;
+  const unsigned char* kpb = reinterpret_cast<const unsigned char*>(a.kp) + (size_t)hk * head_stride_b;
+  const unsigned char* vpb = reinterpret_cast<const unsigned char*>(a.vp) + (size_t)hk * head_stride_b;
+  const size_t blk_row_b = (size_t)a.Hkv * D * sizeof(T);
+  const unsigned char* kbb = reinterpret_cast<const unsigned char*>(a.kb) + (size_t)b * K * blk_row_b +
+                             (size_t)hk * D * sizeof(T);
+  const unsigned char* vbb = reinterpret_cast<const unsigned char*>(a.vb) + (size_t)b * K * blk_row_b +
+                             (size_t)hk * D * sizeof(T);
+  const int lr = lane / CPR, slot = lane % CPR;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int pmask = a.page - 1;
+  const int pfirst = kbeg >> a.page_shift;  // logical page of page_lds[0]
+  // byte offset of the lane's chunk inside its key row for wave load j
+  auto lane_b = [&](int j) { return (uint32_t)((slot ^ TL::swz((j * G + wu) * RPL + lr)) << 4); };
+
+  auto issue = [&](int t, unsigned char* kdst) {
     t = min(t, ntiles - 1);
-    const bool blk = has_blk && (t == ncache_tiles);
     const int base = kbeg + 32 * t;
-    unsigned char* kdst = lds + buf * TL::STAGE_BYTES;
-    unsigned char* vdst = kdst + TL::TILE_BYTES;
+    const bool blk = has_blk && t == ncache_tiles;  // wave-uniform
+    const bool tail = base + 32 > kend;             // wave-uniform
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-      const int idx = (j * G + w) * 64 + lane;
-      const int row = idx / CPR, slot = idx % CPR;
-      const int row0 = __builtin_amdgcn_readfirstlane((j * G + w) * RPL);
-      const int kchunk = slot ^ TL::swz(row);
-      size_t off;
-      const T *ks, *vs;
+      const int row0 = (j * G + wu) * RPL;  // wave-uniform
+      const unsigned char *ksrc, *vsrc;     // wave-uniform bases
+      uint32_t voff;                        // per-lane byte offset
       if (blk) {
-        off = (size_t)min(row, K - 1) * a.Hkv * D;
-        ks = kblk;
-        vs = vblk;
+        ksrc = kbb;
+        vsrc = vbb;
+        voff = (uint32_t)min(row0 + lr, K - 1) * (uint32_t)blk_row_b;
       } else {
         const int p0 = min(base + row0, kend - 1);
-        const int page = page_lds[(p0 - kbeg) / a.page];  // wave-uniform
-        const int p = min(base + row, kend - 1);
-        off = (size_t)page * page_stride + (size_t)hk * head_stride + (size_t)(p % a.page) * D;
-        ks = kpages;
-        vs = vpages;
+        const int page = __builtin_amdgcn_readfirstlane(page_lds[(p0 >> a.page_shift) - pfirst]);
+        const size_t pofs = (size_t)page * page_stride_b;
+        ksrc = kpb + pofs;
+        vsrc = vpb + pofs;
+        const int p = tail ? min(base + row0 + lr, kend - 1) : base + row0 + lr;  // same page as p0
+        voff = (uint32_t)(p & pmask) * ROWB;
       }
-      const int lofs = (j * G + w) * 64 * 16;
-      load_to_lds16(ks + off + kchunk * EPC, kdst + lofs);
-      load_to_lds16(vs + off + kchunk * EPC, vdst + lofs);
+      voff += lane_b(j);
+      const int lofs = (j * G + wu) * 1024;
+      load_to_lds16(ksrc + voff, kdst + lofs);
+      load_to_lds16(vsrc + voff, kdst + TL::TILE_BYTES + lofs);
     }
   };
 
+  // Per-lane LDS byte offsets of the operand reads, relative to a tile.
+  //  K (A operand of S^T): key row r, 16-byte chunk (kk*KSTEP + KW*hh) / EPC, swizzled.
+  //  V^T (A operand of O^T, bf16): two transposed 64-bit reads per 32-column block db; in each
+  //  16-lane group, source lane 4e+q points at (key e, columns 4q..4q+3 of the group's 16), and
+  //  destination lane i receives (key e, column i) for e = 0..3.  Keys of half `hf` of step st
+  //  are 16*st + 8*hf + 4*hh + e (the accumulator rows of P's lane-half hh); the swizzle of those
+  //  rows does not depend on st, so step 1 is step 0 plus 16 rows.
+  const uint32_t lds0 = lds_offset(lds);
+  uint32_t vofs[8];
+  if constexpr (BF) {
+    const int e = (lane >> 2) & 3, q = lane & 3, dgrp = ((lane >> 4) & 1) * 16;
 #pragma unroll
-  for (int st = 0; st < S - 1; ++st) issue(st, st);
-  for (int t = 0; t < ntiles; ++t) {
-    wait_vmcnt<(S - 2) * 2 * NI>();
-    __builtin_amdgcn_s_barrier();  // tile t landed for every wave; tile t-1 fully consumed
-    asm volatile("" ::: "memory");
-    issue(t + S - 1, (t + S - 1) % S);
-    const unsigned char* kt = lds + (t % S) * TL::STAGE_BYTES;
-    const unsigned char* vt = kt + TL::TILE_BYTES;
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int key = 8 * hf + 4 * hh + e;
+        const int d = (db % NDB) * 32 + dgrp + 4 * q;
+        vofs[2 * db + hf] = lds0 + key * ROWB + (((d / EPC) ^ TL::swz(key)) << 4) + (d % EPC) * 2;
+      }
+  }
 
+  auto compute = [&](int t, auto stage_c) {
+    constexpr int ST = decltype(stage_c)::value;
+    constexpr int KOFF = ST * TL::STAGE_BYTES;
+    const unsigned char* kt = lds + KOFF;
+    const unsigned char* vt = kt + TL::TILE_BYTES;
     const bool blk = has_blk && (t == ncache_tiles);
     const int base = kbeg + 32 * t;
-    // S^T tile: rows = keys (lane's A row r), cols = query rows.  Two accumulators over
-    // alternating k-steps (summed once) halve the dependent MFMA chain.
-    f32x16 s0 = f32x16{}, s1 = f32x16{};
+
+    // S^T tile: rows = keys (lane's A row r), cols = query rows.
+    f32x16 sacc = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       typename MF::frag af;
@@ -249,19 +293,17 @@ __global__ __launch_bounds__(64 * G) void attn_kernel(AttnArgs a) {
         const int e = kk * KSTEP + hh;
         af = *reinterpret_cast<const float*>(kt + r * ROWB + (((e / EPC) ^ TL::swz(r)) << 4) + (e % EPC) * 4);
       }
-      if (kk & 1) s1 = MF::mma(af, qf[kk], s1);
-      else s0 = MF::mma(af, qf[kk], s0);
+      sacc = MF::mma(af, qf[kk], sacc);
     }
-    const f32x16 s = s0 + s1;
-    // mask + scale; lane holds query row r, keys acc_row(i, hh).  Tiles that end at or before
-    // the context (every key visible to every row) skip the mask.
+    // Mask; lane holds query row r and keys acc_row(i, hh).  Tiles that end at or before the
+    // context seen by every row skip the mask.
     float sv[16];
     float mt = kNegInf;
     const bool full = !blk && (base + 32 <= (DRAFT ? kend : min(kend, n + 1)));
     if (full) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        sv[i] = s[i] * a.scale_log2;
+        sv[i] = sacc[i];
         mt = fmaxf(mt, sv[i]);
       }
     } else {
@@ -270,73 +312,61 @@ __global__ __launch_bounds__(64 * G) void attn_kernel(AttnArgs a) {
         const int kl = acc_row(i, hh);
         const int p = base + kl;
         const bool ok = blk ? (kl < K) : ((p < kend) && (DRAFT || p <= n + r));
-        sv[i] = ok ? s[i] * a.scale_log2 : kNegInf;
+        sv[i] = ok ? sacc[i] : kNegInf;
         mt = fmaxf(mt, sv[i]);
       }
     }
-    mt = fmaxf(mt, shfl_xor_f(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    mt = fmaxf(mt, shfl_xor_f(mt, 32)) * csc;  // the row's tile maximum, log2 units (scale > 0)
+    const bool raise = mt > m_run + kLazy;
+    if (__any(raise)) {
+      const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+      m_run = raise ? mt : m_run;
+    }
+    const float m_use = (m_run == kNegInf) ? 0.0f : m_run;
     float p[16];
     float lsum = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      p[i] = __builtin_amdgcn_exp2f(sv[i] - m_use);
+      p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], csc, -m_use));
       lsum += p[i];
     }
-    l_run = l_run * alpha + lsum;
-    // rescale only when some row's max moved (alpha == 1 exactly otherwise, and x * 1 == x)
-    if (__any(m_new != m_run)) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-    }
-    m_run = m_new;
+    l_run += lsum;
 
-    // O^T += V^T P^T with V stored row = key (chunk-swizzled like K).  bf16 operands: P is split
-    // into hi + lo bf16 terms (P - hi rounded again), so the product carries ~16 mantissa bits of
-    // P instead of 8 and the attention output stays near fp32 accuracy.  The V^T fragment (lane:
-    // column d = 32*db + r, 8 keys) comes from two transposed 64-bit LDS reads: in each 16-lane
-    // group, source lane 4e+q points at (key e, columns 4q..4q+3 of the group's 16) and
-    // destination lane i receives (key e, column i) for e = 0..3.
-    auto vaddr = [&](int key, int d) -> const unsigned char* {
-      return vt + key * ROWB + (((d / EPC) ^ TL::swz(key)) << 4) + (d % EPC) * (int)sizeof(T);
-    };
+    // O^T += V^T P^T.  bf16: P enters as hi + lo bf16 terms (hi = P truncated to bf16, lo = the
+    // exact remainder rounded to bf16), ~16 mantissa bits of P instead of 8.
     if constexpr (BF) {
+      static_assert(NDB <= 4, "eight transposed reads cover four 32-column blocks");
+      static_for<2>([&](auto stc) {
+        constexpr int st = decltype(stc)::value;
+        u32x4 hi4;
+        bf16x8 pl;
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        bf16x8 ph, pl;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float pv = p[8 * st + j];
-          const bf16 h = (bf16)pv;
-          ph[j] = h;
-          pl[j] = (bf16)(pv - (float)h);
+        for (int j = 0; j < 4; ++j) {
+          const float p0 = p[8 * st + 2 * j], p1 = p[8 * st + 2 * j + 1];
+          const uint32_t u0 = __float_as_uint(p0) & 0xffff0000u, u1 = __float_as_uint(p1) & 0xffff0000u;
+          hi4[j] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+          pl[2 * j] = (bf16)(p0 - __uint_as_float(u0));
+          pl[2 * j + 1] = (bf16)(p1 - __uint_as_float(u1));
         }
-        (void)pl;
-        const int e = (lane >> 2) & 3, q = lane & 3, dgrp = ((lane >> 4) & 1) * 16;
-        static_assert(NDB <= 4, "eight transposed reads cover four 32-column blocks");
-        uint32_t va[8];
+        const bf16x8 ph = __builtin_bit_cast(bf16x8, hi4);
         u32x2 vr[8];
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int d = (db % NDB) * 32 + dgrp + 4 * q;
-          va[2 * db] = lds_offset(vaddr(acc_row(8 * st + e, hh), d));
-          va[2 * db + 1] = lds_offset(vaddr(acc_row(8 * st + 4 + e, hh), d));
-        }
-        read_tr16_x8(va, vr);
+        read_tr16_x8_at<KOFF + TL::TILE_BYTES + st * 16 * ROWB>(vofs, vr);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const bf16x4 lo4 = __builtin_bit_cast(bf16x4, vr[2 * db]);
-          const bf16x4 hi4 = __builtin_bit_cast(bf16x4, vr[2 * db + 1]);
-          const bf16x8 vf = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+          const bf16x4 hi4v = __builtin_bit_cast(bf16x4, vr[2 * db + 1]);
+          const bf16x8 vf = {lo4[0], lo4[1], lo4[2], lo4[3], hi4v[0], hi4v[1], hi4v[2], hi4v[3]};
           o[db] = MF::mma(vf, ph, o[db]);
-#ifndef ORTHRUS_ATTN_P_BF16_ONLY
           o[db] = MF::mma(vf, pl, o[db]);
-#endif
         }
-      }
+      });
     } else {
+      auto vaddr = [&](int key, int d) -> const unsigned char* {
+        return vt + key * ROWB + (((d / EPC) ^ TL::swz(key)) << 4) + (d % EPC) * (int)sizeof(T);
+      };
 #pragma unroll
       for (int st = 0; st < 16; ++st) {
         const int key = acc_row(st, hh);
@@ -345,6 +375,25 @@ __global__ __launch_bounds__(64 * G) void attn_kernel(AttnArgs a) {
           o[db] = MF::mma(*reinterpret_cast<const float*>(vaddr(key, db * 32 + r)), p[st], o[db]);
       }
     }
+  };
+
+  // Ring of S stages, loop unrolled by S so that every LDS address is a per-lane register plus an
+  // immediate.  Iteration t: tile t has landed once at most S-2 tiles' loads are outstanding; the
+  // barrier also tells every wave that tile t-1 (whose stage the next issue overwrites) is done.
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st) issue(st, lds + st * TL::STAGE_BYTES);
+  for (int t0 = 0; t0 < ntiles; t0 += S) {
+    static_for<S>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      const int t = t0 + s;
+      if (t < ntiles) {
+        wait_vmcnt<(S - 2) * 2 * NI>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        issue(t + S - 1, lds + ((s + S - 1) % S) * TL::STAGE_BYTES);
+        compute(t, sc);
+      }
+    });
   }
 
   const float l_tot = l_run + shfl_xor_f(l_run, 32);
@@ -425,6 +474,8 @@ int32_t validate(const orthrus_attn_desc_t* d) {
   ORTHRUS_REQUIRE(d->head_dim == 64 || d->head_dim == 128, ORTHRUS_ERR_UNSUPPORTED, "attn: head_dim %d", d->head_dim);
   ORTHRUS_REQUIRE(d->block >= 1 && d->block <= 32, ORTHRUS_ERR_INVALID_ARG, "attn: block %d not in 1..32", d->block);
   ORTHRUS_REQUIRE(d->page_size >= 1 && d->max_pages >= 1, ORTHRUS_ERR_INVALID_ARG, "attn: bad paging");
+  ORTHRUS_REQUIRE((d->page_size & (d->page_size - 1)) == 0, ORTHRUS_ERR_UNSUPPORTED,
+                  "attn: page_size %d is not a power of two", d->page_size);
   {
     const int cpr = d->head_dim * (d->dtype == ORTHRUS_BF16 ? 2 : 4) / 16;  // 16-byte chunks per key row
     const int rows_per_load = 64 / cpr;
@@ -441,7 +492,8 @@ int32_t validate(const orthrus_attn_desc_t* d) {
   ORTHRUS_REQUIRE(valid_dtype(d->dtype) && valid_dtype(d->out_dtype), ORTHRUS_ERR_INVALID_ARG, "attn: bad dtype");
   ORTHRUS_REQUIRE(!(d->dtype == ORTHRUS_F32 && d->out_dtype == ORTHRUS_BF16), ORTHRUS_ERR_UNSUPPORTED,
                   "attn: fp32 inputs with bf16 output not built");
-  ORTHRUS_REQUIRE(std::isfinite(d->scale), ORTHRUS_ERR_INVALID_ARG, "attn: scale not finite");
+  ORTHRUS_REQUIRE(std::isfinite(d->scale) && d->scale > 0.0f, ORTHRUS_ERR_INVALID_ARG,
+                  "attn: scale must be finite and positive");
   return ORTHRUS_OK;
 }
 
@@ -486,6 +538,7 @@ int32_t run(const orthrus_attn_desc_t* d, const void* q, const void* kp, const v
   a.part_acc = reinterpret_cast<float*>(ws);
   a.part_ml = a.nchunk_max > 1 ? a.part_acc + acc_elems : nullptr;
   a.Hq = d->q_heads; a.Hkv = d->kv_heads; a.K = d->block; a.page = d->page_size; a.max_pages = d->max_pages;
+  a.page_shift = __builtin_ctz((unsigned)d->page_size);
   a.max_ctx = d->max_ctx; a.chunk = chunk_of(d); a.scale_log2 = d->scale * kLog2e;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (d->head_dim == 128) {
