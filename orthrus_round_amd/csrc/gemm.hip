@@ -18,30 +18,24 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, cons
   xcd_tile_map(blockIdx.x, gridDim.x, 1, mtiles, sp, mt, nt);
   const int m0 = mt * Cfg::BM, n0 = nt * Cfg::BN;
   f32x16 acc[Cfg::TM][Cfg::TN];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hh = lane >> 5, r = lane & 31;
-  if constexpr (Cfg::KSPLIT) {
-    gemm_mainloop_ks4<T, Cfg>(A, W, M, N, K, m0, n0, smem, acc);
-  } else {
-    gemm_mainloop<T, Cfg>(A, W, M, N, K, m0, n0, 0, K, smem, acc);
-  }
-  // block (i, j) of the tile: k-split tiles sum the four wave partials from LDS, plain tiles
-  // hold it in this wave's registers (wave (wm, wn) owns blocks i in [wm*TM, ..), j in [wn*TN, ..))
+  const int lane = threadIdx.x & 63, hh = lane >> 5, r = lane & 31;
+  const int wu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  gemm_mainloop<T, Cfg>(A, W, M, N, K, m0, n0, smem, acc);
+  constexpr int NBI = Cfg::BM / 32, NBJ = Cfg::BN / 32;
+  if constexpr (!Cfg::KSPLIT) park_plain<Cfg>(smem, acc);
+  // the tile's 32x32 blocks are now in LDS (k-split: four partials each); wave q % 4 stores block q
   auto block = [&](int i, int j) -> f32x16 {
     if constexpr (Cfg::KSPLIT) return ks4_sum<Cfg>(smem, i, j);
-    else return acc[i - (w / Cfg::WN) * Cfg::TM][j - (w % Cfg::WN) * Cfg::TN];
-  };
-  auto owns = [&](int q, int i, int j) -> bool {
-    if constexpr (Cfg::KSPLIT) return q % 4 == w;
-    else return i / Cfg::TM == w / Cfg::WN && j / Cfg::TN == w % Cfg::WN;
+    else return plain_block<Cfg>(smem, i, j);
   };
   if constexpr (EPI == ORTHRUS_EPI_SWIGLU) {
     // columns come in (gate 32, up 32) pairs: block j even = gate, j+1 = its up block
     const int NO = N / 2;
 #pragma unroll
-    for (int i = 0; i < Cfg::BM / 32; ++i)
+    for (int i = 0; i < NBI; ++i)
 #pragma unroll
-      for (int j = 0; j < Cfg::BN / 32; j += 2) {
-        if (!owns(i * (Cfg::BN / 64) + j / 2, i, j)) continue;
+      for (int j = 0; j < NBJ; j += 2) {
+        if ((i * (NBJ / 2) + j / 2) % 4 != wu) continue;
         const int ng = n0 + j * 32;  // multiple of 64
         if (ng >= N) continue;
         const f32x16 g = block(i, j), u = block(i, j + 1);
@@ -50,17 +44,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, cons
         for (int e = 0; e < 16; ++e) {
           const int m = m0 + i * 32 + acc_row(e, hh);
           if (m < M) {
-            const float s = g[e] / (1.0f + expf(-g[e]));
-            C[(size_t)m * NO + col] = from_f32<OutT>(s * u[e]);
+            const float sg = g[e] / (1.0f + expf(-g[e]));
+            C[(size_t)m * NO + col] = from_f32<OutT>(sg * u[e]);
           }
         }
       }
   } else {
 #pragma unroll
-    for (int i = 0; i < Cfg::BM / 32; ++i)
+    for (int i = 0; i < NBI; ++i)
 #pragma unroll
-      for (int j = 0; j < Cfg::BN / 32; ++j) {
-        if (!owns(i * (Cfg::BN / 32) + j, i, j)) continue;
+      for (int j = 0; j < NBJ; ++j) {
+        if ((i * NBJ + j) % 4 != wu) continue;
         const int n = n0 + j * 32 + r;
         if (n >= N) continue;
         const f32x16 v = block(i, j);
@@ -81,12 +75,25 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, cons
 //  * N < 16384 (QKV, O, down projections): KsCfg tiles, k-steps split four ways per workgroup;
 //  * N >= 16384 (the gate/up projection): plain GemmCfg tiles, waves split the output tile.
 // Within a family the tile height follows M only to avoid idle rows.
-template <typename T> using KsSmall = KsCfg<T, 32, 64, 6>;
-template <typename T> using KsBig = KsCfg<T, 64, 64, 4>;
-template <typename T> using KsBigDeep = KsCfg<T, 64, 64, 6>;  // long reductions (K > 8192)
-template <typename T> using PlainSmall = GemmCfg<T, 32, 128, 1, 4, 4>;
-template <typename T> using PlainMid = GemmCfg<T, 64, 128, 2, 2, 3>;
-template <typename T> using PlainBig = GemmCfg<T, 128, 128, 2, 2, 2>;
+// Ring depths (A stages, W stages) keep each configuration at or under 80 KiB of LDS, so two
+// workgroups share a CU, with the deeper ring on the weight stream.
+#ifndef ORTHRUS_KSS_RINGS
+#define ORTHRUS_KSS_RINGS 6, 6
+#endif
+#ifndef ORTHRUS_KSB_RINGS
+#define ORTHRUS_KSB_RINGS 5, 5
+#endif
+#ifndef ORTHRUS_PB_RINGS
+#define ORTHRUS_PB_RINGS 3, 2
+#endif
+template <typename T> using KsSmall = KsCfg<T, 32, 64, ORTHRUS_KSS_RINGS>;
+template <typename T> using KsBig = KsCfg<T, 64, 64, ORTHRUS_KSB_RINGS>;
+template <typename T> using PlainSmall = GemmCfg<T, 32, 128, 1, 4, 4, 4>;
+template <typename T> using PlainMid = GemmCfg<T, 64, 128, 2, 2, 3, 3>;
+template <typename T> using PlainBig = GemmCfg<T, 128, 128, 2, 2, ORTHRUS_PB_RINGS>;
+#ifndef ORTHRUS_WIDE_BIG_CFG
+#define ORTHRUS_WIDE_BIG_CFG(T) PlainBig<T>
+#endif
 constexpr int kWideN = 16384;
 
 template <typename T, typename OutT, typename Cfg>
@@ -122,12 +129,11 @@ template <typename T, typename OutT>
 int32_t launch(int M, int N, int K, int epi, const void* a, const void* w, const void* res, void* c, hipStream_t st) {
   if (N < kWideN) {
     if (M <= 32) return launch_cfg<T, OutT, KsSmall<T>>(M, N, K, epi, a, w, res, c, st);
-    if (K > 8192) return launch_cfg<T, OutT, KsBigDeep<T>>(M, N, K, epi, a, w, res, c, st);
     return launch_cfg<T, OutT, KsBig<T>>(M, N, K, epi, a, w, res, c, st);
   }
   if (M <= 32) return launch_cfg<T, OutT, PlainSmall<T>>(M, N, K, epi, a, w, res, c, st);
   if (M <= 64) return launch_cfg<T, OutT, PlainMid<T>>(M, N, K, epi, a, w, res, c, st);
-  return launch_cfg<T, OutT, PlainBig<T>>(M, N, K, epi, a, w, res, c, st);
+  return launch_cfg<T, OutT, ORTHRUS_WIDE_BIG_CFG(T)>(M, N, K, epi, a, w, res, c, st);
 }
 
 template <typename T>

@@ -39,8 +39,8 @@ __global__ __launch_bounds__(256) void lmhead_kernel(LmArgs a) {
   xcd_tile_map(blockIdx.x, gridDim.x, 1, mtiles, sp, mt, nt);
   const int m0 = mt * Cfg::BM, n0 = nt * Cfg::BN;
   f32x16 acc[Cfg::TM][Cfg::TN];
-  gemm_mainloop<T, Cfg>(reinterpret_cast<const T*>(a.h), reinterpret_cast<const T*>(a.w), a.M, a.N, a.K, m0, n0, 0, a.K,
-                        smem, acc);
+  gemm_mainloop<T, Cfg>(reinterpret_cast<const T*>(a.h), reinterpret_cast<const T*>(a.w), a.M, a.N, a.K, m0, n0, smem,
+                        acc);
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hh = lane >> 5, r = lane & 31;
   const int wm = w / Cfg::WN, wn = w % Cfg::WN;
@@ -154,6 +154,9 @@ int32_t launch(LmArgs& a, hipStream_t st) {
 }
 
 constexpr int kLmBN = 128;
+#ifndef ORTHRUS_LM_BIG_CFG
+#define ORTHRUS_LM_BIG_CFG(T) GemmCfg<T, 128, kLmBN, 2, 2, 3, 2>
+#endif
 
 }  // namespace
 }  // namespace orthrus
@@ -196,13 +199,13 @@ extern "C" int32_t orthrus_lmhead_argmax(const orthrus_lmhead_desc_t* d, const v
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   int32_t s;
   if (d->dtype == ORTHRUS_BF16) {
-    if (a.M <= 32) s = launch<bf16, GemmCfg<bf16, 32, kLmBN, 1, 4, 4>>(a, st);
-    else if (a.M <= 64) s = launch<bf16, GemmCfg<bf16, 64, kLmBN, 2, 2, 3>>(a, st);
-    else s = launch<bf16, GemmCfg<bf16, 128, kLmBN, 2, 2, 2>>(a, st);
+    if (a.M <= 32) s = launch<bf16, GemmCfg<bf16, 32, kLmBN, 1, 4, 4, 4>>(a, st);
+    else if (a.M <= 64) s = launch<bf16, GemmCfg<bf16, 64, kLmBN, 2, 2, 3, 3>>(a, st);
+    else s = launch<bf16, ORTHRUS_LM_BIG_CFG(bf16)>(a, st);
   } else {
-    if (a.M <= 32) s = launch<float, GemmCfg<float, 32, kLmBN, 1, 4, 4>>(a, st);
-    else if (a.M <= 64) s = launch<float, GemmCfg<float, 64, kLmBN, 2, 2, 3>>(a, st);
-    else s = launch<float, GemmCfg<float, 128, kLmBN, 2, 2, 2>>(a, st);
+    if (a.M <= 32) s = launch<float, GemmCfg<float, 32, kLmBN, 1, 4, 4, 4>>(a, st);
+    else if (a.M <= 64) s = launch<float, GemmCfg<float, 64, kLmBN, 2, 2, 3, 3>>(a, st);
+    else s = launch<float, ORTHRUS_LM_BIG_CFG(float)>(a, st);
   }
   if (s != ORTHRUS_OK) return s;
   hipLaunchKernelGGL(lmhead_finalize, dim3(a.M), dim3(64), 0, st, a.part_best, a.part_m, a.part_s, a.ntiles, token_out,

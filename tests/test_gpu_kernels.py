@@ -268,7 +268,8 @@ def test_philox_words_match_numpy():
 
 @pytest.mark.parametrize("dtype", [ora.BF16, ora.F32])
 @pytest.mark.parametrize("M,N,K", [(256, 6144, 4096), (8, 4096, 4096), (45, 1024, 256), (100, 320, 128),
-                                   (256, 16384, 256), (40, 16448, 128)])
+                                   (256, 16384, 256), (40, 16448, 128), (8, 16384, 256), (32, 24576, 192),
+                                   (70, 16512, 64)])
 @pytest.mark.parametrize("epi", [ora.EPI_STORE, ora.EPI_RESIDUAL, ora.EPI_SWIGLU])
 def test_gemm_epilogues(dtype, M, N, K, epi):
     if epi == ora.EPI_SWIGLU and N % 64:
