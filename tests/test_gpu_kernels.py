@@ -316,14 +316,22 @@ def test_gemm_row_invariance(dtype, N):
 
 
 @pytest.mark.parametrize("dtype", [ora.BF16, ora.F32])
-def test_rmsnorm(dtype):
+@pytest.mark.parametrize("hidden,offset", [(4096, 0), (256, 0), (1004, 0), (8200, 0), (4096, 1)])
+def test_rmsnorm(dtype, hidden, offset):
+    """Register-resident 16-byte path (aligned rows up to 1024 chunks per row), and the scalar
+    path for ragged widths, very wide rows and tensors not 16-byte aligned (offset)."""
     bf = dtype == ora.BF16
-    x = synth.lmhead_inputs(23, 33, 4096, 8, h_std=3.0, bf16=bf)[0]
-    g = (1 + 0.1 * np.random.default_rng(1).standard_normal(4096)).astype(np.float32)
-    y = torch.empty((33, 4096), dtype=torch.bfloat16 if bf else torch.float32, device=DEV)
-    ora.rmsnorm(33, 4096, dtype, dev(x, dtype), dev(g), 1e-6, y)
+    rows = 33
+    x = synth.lmhead_inputs(23, rows, hidden, 8, h_std=3.0, bf16=bf)[0]
+    g = (1 + 0.1 * np.random.default_rng(1).standard_normal(hidden)).astype(np.float32)
+    tdt = torch.bfloat16 if bf else torch.float32
+    xs = torch.zeros(rows * hidden + offset, dtype=tdt, device=DEV)
+    xs[offset:] = dev(x, dtype).reshape(-1)
+    ys = torch.empty(rows * hidden + offset, dtype=tdt, device=DEV)
+    y = ys[offset:]
+    ora.rmsnorm(rows, hidden, dtype, xs[offset:], dev(g), 1e-6, y)
     ref = M.rmsnorm(x.astype(np.float64), g.astype(np.float64), 1e-6)
-    err = np.abs(y.float().cpu().numpy() - ref).max() / np.abs(ref).max()
+    err = np.abs(y.float().cpu().numpy().reshape(rows, hidden) - ref).max() / np.abs(ref).max()
     assert err <= (4e-3 if bf else 1e-6)
 
 
