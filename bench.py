@@ -33,6 +33,8 @@ def parse():
     p.add_argument("--kv-chunk", type=int, default=640)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-attn", action="store_true")
+    p.add_argument("--no-extras", action="store_true", help="skip the block sweep and trajectory match")
+    p.add_argument("--match-tokens", type=int, default=64)
     return p.parse_args()
 
 
@@ -226,6 +228,48 @@ def cpu_baseline(W, shape, prompts_np, tokens_per_round_seq, kv_seed=9):
             "round_s": round(full_round, 3)}
 
 
+def block_sweep(dec, prompts, blocks=(4, 8, 16, 32), rounds=12):
+    """Round latency (graph replay, ms) of the same model and context for each block size."""
+    import torch
+    res = {}
+    for K in blocks:
+        dec.set_block(K)
+        dec.prefill(torch.from_numpy(prompts), max_out=32 * (rounds + 4))
+        g = dec.capture(dec.round_greedy)
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(rounds):
+            g.replay()
+        torch.cuda.synchronize()
+        res[str(K)] = round((time.perf_counter() - t0) / rounds * 1e3, 4)
+        del g
+    dec.set_block(dec.block_alloc)
+    return res
+
+
+def trajectory_match(dec, W, shape, prompts, n_tokens, kv_chunk):
+    """Greedy Orthrus vs greedy AR through the same kernels: fraction of sequences whose first
+    n_tokens agree exactly, in bf16 (the timed decoder) and fp32 (the same bf16-valued weights
+    held in fp32)."""
+    import torch
+    from orthrus_round_amd.decoder import Decoder
+    B = prompts.shape[0]
+    out = {}
+    for prec in ("bf16", "fp32"):
+        d = dec if prec == "bf16" else Decoder(W, shape, precision="fp32", block=32, max_batch=B,
+                                                max_ctx=prompts.shape[1] + n_tokens + 96, kv_chunk=kv_chunk)
+        a, st = d.generate(prompts, n_tokens, use_graph=True)
+        b, _ = d.generate_ar(prompts, n_tokens, use_graph=True)
+        same = [bool(np.array_equal(a[i], b[i])) for i in range(B)]
+        out[prec] = {"match_rate": sum(same) / B, "sequences": B, "tokens": n_tokens, "rounds": st.rounds}
+        if d is not dec:
+            del d
+            torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -285,6 +329,10 @@ def main():
     torch.cuda.synchronize()
     ar_ms = (time.perf_counter() - ta) / 20 * 1e3
 
+    sweep = match = None
+    if not args.no_extras:
+        sweep = block_sweep(dec, prompts)
+        match = trajectory_match(dec, W, shape, prompts, args.match_tokens, args.kv_chunk)
     attn = None if args.no_attn else attention_roofline(1024)
     # calibration for HBM-traffic counters: one plain 256 MiB device copy
     cal_src = torch.ones(256 * 2**20, dtype=torch.uint8, device="cuda")
@@ -326,6 +374,8 @@ def main():
         "kernels": {k: {"ms": round(v["ms"], 5), "per_round": v["per_round"],
                         "GBs": round(v["bytes"] / v["ms"] / 1e6, 1)} for k, v in tab.items()},
         "attention_roofline": attn,
+        "round_ms_by_block": sweep,
+        "trajectory_match_vs_ar": match,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -54,7 +54,8 @@ class Decoder:
                  page_order_seed: int | None = None):
         L.lib()  # fail loudly if the HIP library is missing
         self.shape = s = shape
-        self.K = block
+        self.K = block            # rows per sequence of a round (set_block may lower it)
+        self.block_alloc = block  # rows per sequence the buffers hold; also the prefill chunk
         self.B = max_batch
         self.dev = torch.device(device)
         self.prec = precision
@@ -179,13 +180,23 @@ class Decoder:
         L.lmhead_argmax(d, self.a[:M], self.lm_head, self.seq_id, self.round, tokens, logits, lse, self.lm_ws)
 
     # ------------------------------------------------------------------ prefill / state
+    def set_block(self, block: int):
+        """Use rounds of `block` rows per sequence (1 <= block <= the block the buffers were built
+        for).  Round buffers are used as flat arrays of batch*block rows, so they serve any smaller
+        block; graphs captured for another block must be captured again."""
+        assert 1 <= block <= self.block_alloc
+        self.K = block
+        self._logits = None
+        self.graph = None
+
     def prefill(self, prompts: torch.Tensor, max_out: int):
-        """AR prefill of prompts[:, :-1] in K-row causal chunks; anchor := prompts[:, -1]."""
+        """AR prefill of prompts[:, :-1] in causal chunks of the allocated block; anchor :=
+        prompts[:, -1].  Every kernel's per-row result is independent of the chunking."""
         B, P = prompts.shape
         assert B == self.B and P >= 1 and P - 1 + self.K <= self.max_ctx
         prompts = prompts.to(self.dev, torch.int32).contiguous()
-        for c in range(0, P - 1, self.K):
-            kb = min(self.K, P - 1 - c)
+        for c in range(0, P - 1, self.block_alloc):
+            kb = min(self.block_alloc, P - 1 - c)
             ctx = torch.full((B,), c, dtype=torch.int32, device=self.dev)
             L.embed_block(B, kb, self.shape.hidden, self.dt, self.embed, None, prompts, P, c, self.shape.mask_id,
                           self.x)

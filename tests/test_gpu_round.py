@@ -47,6 +47,20 @@ def test_tiny_fp32_trajectory_and_accepts_match_oracle(tiny, prompts):
     print(f"rounds {st.rounds} tpf {st.tpf:.3f}")
 
 
+@pytest.mark.parametrize("block", [8, 1])
+def test_smaller_block_matches_oracle(tiny, prompts, block):
+    """A decoder built for 32-row rounds, switched to `block` rows: tokens and per-round accepts
+    equal the oracle's Orthrus run with the same block (block 1 is plain AR decoding)."""
+    W, Wt = tiny
+    dec = make(W)
+    dec.set_block(block)
+    toks, st = dec.generate(prompts[:1], 96, poll_every=1, record_accepts=True)
+    ref = Dc.generate(Wt, prompts[0], 96, block=block)
+    assert list(toks[0]) == ref.tokens
+    assert [int(h[0]) for h in st.accept_hist[: len(ref.rounds)]] == [r.accept for r in ref.rounds]
+    assert int(dec.ctx_len[0]) == 63 + sum(len(r.emitted) for r in ref.rounds)
+
+
 @pytest.mark.parametrize("precision", ["fp32", "bf16"])
 def test_orthrus_equals_ar_on_gpu(tiny, prompts, precision):
     W, _ = tiny
