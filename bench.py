@@ -34,6 +34,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-attn", action="store_true")
     p.add_argument("--no-extras", action="store_true", help="skip the block sweep and trajectory match")
+    p.add_argument("--counters", action="store_true",
+                   help="hardware-counter mode: prefill, the timed rounds and the calibration copy only")
     p.add_argument("--match-tokens", type=int, default=64)
     return p.parse_args()
 
@@ -228,6 +230,17 @@ def cpu_baseline(W, shape, prompts_np, tokens_per_round_seq, kv_seed=9):
             "round_s": round(full_round, 3)}
 
 
+def calibration_copy():
+    """One plain 256 MiB device-to-device copy: the reference dispatch that scales the HBM
+    traffic counters (FETCH_SIZE / WRITE_SIZE) to bytes."""
+    import torch
+    cal_src = torch.ones(256 * 2**20, dtype=torch.uint8, device="cuda")
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    torch.cuda.synchronize()
+    del cal_src, cal_dst
+
+
 def block_sweep(dec, prompts, blocks=(4, 8, 16, 32), rounds=12):
     """Round latency (graph replay, ms) of the same model and context for each block size."""
     import torch
@@ -311,6 +324,11 @@ def main():
     ctx_np = dec.ctx_len.cpu().numpy()
     print(f"[bench] {args.steps} rounds in {elapsed:.3f}s, committed {committed}", file=sys.stderr, flush=True)
 
+    if args.counters:
+        calibration_copy()
+        print(json.dumps({"mode": "counters", "rounds": args.steps, "ms_per_step": round(elapsed / args.steps * 1e3, 4)}),
+              flush=True)
+        return
     tab = kernel_table(dec, ctx_np)
     per_round = {k: v["ms"] * v["per_round"] for k, v in tab.items()}
     dominant = max(per_round, key=per_round.get)
@@ -334,12 +352,7 @@ def main():
         sweep = block_sweep(dec, prompts)
         match = trajectory_match(dec, W, shape, prompts, args.match_tokens, args.kv_chunk)
     attn = None if args.no_attn else attention_roofline(1024)
-    # calibration for HBM-traffic counters: one plain 256 MiB device copy
-    cal_src = torch.ones(256 * 2**20, dtype=torch.uint8, device="cuda")
-    cal_dst = torch.empty_like(cal_src)
-    cal_dst.copy_(cal_src)
-    torch.cuda.synchronize()
-    del cal_src, cal_dst
+    calibration_copy()
     tokens_per_round_seq = committed / (args.steps * args.batch)
     cpu = None
     if not args.no_cpu_baseline:
