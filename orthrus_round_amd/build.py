@@ -21,7 +21,10 @@ FLAGS = [
 ]
 # Per-source flags.  attn.hip keeps its MFMA accumulators in ordinary VGPRs: the online-softmax
 # rescale works on them with vector ALU instructions, which cannot address accumulation registers.
-EXTRA = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# MFMA accumulators in ordinary VGPRs: the unified register file then has one budget instead of
+# a fixed VGPR/AGPR split, which spilled the pipelined GEMM main loop.
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+EXTRA = {"attn.hip": _VGPR_FORM, "gemm.hip": _VGPR_FORM, "lmhead.hip": _VGPR_FORM}
 
 
 def build(verbose: bool = False, jobs: int = 6) -> str:

@@ -67,14 +67,6 @@ template <int N> __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int I> struct Int { static constexpr int value = I; };
-template <int N, int I = 0, typename F> __device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(Int<I>{});
-    static_for<N, I + 1>(f);
-  }
-}
-
 // Eight gfx950 transposed LDS reads (ds_read_b64_tr_b16: 64 bits per lane, transposed within
 // groups of 16 lanes) and the wait for them, in one asm block: the compiler cannot pair the
 // builtin with the direct global->LDS tile loads and would drain every load in flight first.

@@ -35,6 +35,15 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf
 // The 16 accumulator values of lane l belong to column l%32 and rows
 // (i/4)*8 + (l/32)*4 + i%4, i = 0..15.
 // ---------------------------------------------------------------------------------------
+// Compile-time loop: f(Int<0>{}), ..., f(Int<N-1>{}), so that indices stay constants.
+template <int I> struct Int { static constexpr int value = I; };
+template <int N, int I = 0, typename F> __device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(Int<I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
 template <typename T> struct Mfma;
 
 template <> struct Mfma<bf16> {

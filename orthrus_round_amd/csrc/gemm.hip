@@ -10,7 +10,7 @@ namespace orthrus {
 namespace {
 
 template <typename T, typename OutT, typename Cfg, int EPI>
-__global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, const T* __restrict__ W,
+__global__ __launch_bounds__(256) ORTHRUS_GEMM_WAVES void gemm_kernel(const T* __restrict__ A, const T* __restrict__ W,
                                                    const OutT* residual, OutT* C, int M, int N, int K) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int mtiles = (M + Cfg::BM - 1) / Cfg::BM;

@@ -23,6 +23,18 @@
 
 #include "common.hpp"
 
+// The rings take up to 80 KiB of LDS, so at most two workgroups (two waves per SIMD) share a CU:
+// tell the compiler, so that it spends the registers that occupancy leaves free on keeping a
+// stage's fragments in flight instead of minimising them.
+// MFMAs per software-pipeline part of the plain layout (see gemm_mainloop)
+#ifndef ORTHRUS_PART_MFMAS
+#define ORTHRUS_PART_MFMAS 8
+#endif
+
+#ifndef ORTHRUS_GEMM_WAVES
+#define ORTHRUS_GEMM_WAVES __attribute__((amdgpu_waves_per_eu(1, 2)))
+#endif
+
 namespace orthrus {
 
 template <typename T, int BM_, int BN_, int SA_, int SW_>
@@ -105,6 +117,18 @@ __device__ __forceinline__ void load_to_lds16(const void* src, unsigned char* ds
   __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
 }
 
+// Stage kt of one role's ring: load j of wave wl fills tile rows (2j + wl)*8 .. +7 of slot kt % S.
+// Takes its state by value: lambdas capturing the per-lane pointers by reference were left in
+// scratch memory by the compiler when the two rings differ in depth.
+template <int S, int NL, int STAGE, int BK, typename T>
+__device__ __forceinline__ void issue_stage(const T* src0, int row0, int lim, int K, unsigned char* ring, int kt,
+                                            int wl) {
+  unsigned char* dst = ring + (kt % S) * STAGE;
+#pragma unroll
+  for (int j = 0; j < NL; ++j)
+    load_to_lds16(src0 + (size_t)min(row0 + 16 * j, lim) * K + (size_t)kt * BK, dst + (2 * j + wl) * 8 * 128);
+}
+
 // Shared main loop.  On return acc holds this wave's accumulators: its WM x WN share of the tile
 // (plain), or its k-quarter partial of the whole tile, already parked in LDS for ks4_sum (k-split).
 template <typename T, typename Cfg, typename Acc>
@@ -131,26 +155,19 @@ __device__ __forceinline__ void gemm_mainloop(const T* __restrict__ A, const T* 
   // wl fills tile rows (2j + wl)*8 .. +7; lane l lands in row +l/8, slot l%8, and fetches the chunk
   // that slot holds under the swizzle.  Rows past M or N read a clamped valid row: those outputs
   // are never stored.
-  constexpr int NLMAX = NLA > NLW ? NLA : NLW;
-  const T* src[NLMAX];
-#pragma unroll
-  for (int j = 0; j < NLMAX; ++j) {
-    const int trow = (2 * j + wl) * 8 + (lane >> 3);
-    const int chunk = (lane & 7) ^ lds_swizzle(trow);
-    const T* base = w_role ? W + (size_t)min(n0 + trow, N - 1) * K : A + (size_t)min(m0 + trow, M - 1) * K;
-    src[j] = base + chunk * EPC;
-  }
-  auto issue_a = [&](int kt) {
-    unsigned char* dst = ring_a + (kt % SA) * Cfg::A_STAGE;
-#pragma unroll
-    for (int j = 0; j < NLA; ++j) load_to_lds16(src[j] + (size_t)kt * BK, dst + (2 * j + wl) * 8 * ROWB);
+  // Row trow = 16j + 8wl + l/8 has swizzle (trow/2) mod 8 = (4wl + l/16) mod 8 for every j.
+  // The row offset is recomputed per load: an array of per-load pointers ends up in scratch.
+  const T* const mat = w_role ? W : A;
+  const int lim = (w_role ? N : M) - 1;
+  const int row0 = (w_role ? n0 : m0) + wl * 8 + (lane >> 3);
+  const T* const src0 = mat + ((lane & 7) ^ lds_swizzle(wl * 8 + (lane >> 3))) * EPC;
+  auto issue_a = [&](int kt) __attribute__((always_inline)) {
+    issue_stage<SA, NLA, Cfg::A_STAGE, BK>(src0, row0, lim, K, ring_a, kt, wl);
   };
-  auto issue_w = [&](int kt) {
-    unsigned char* dst = ring_w + (kt % SW) * Cfg::W_STAGE;
-#pragma unroll
-    for (int j = 0; j < NLW; ++j) load_to_lds16(src[j] + (size_t)kt * BK, dst + (2 * j + wl) * 8 * ROWB);
+  auto issue_w = [&](int kt) __attribute__((always_inline)) {
+    issue_stage<SW, NLW, Cfg::W_STAGE, BK>(src0, row0, lim, K, ring_w, kt, wl);
   };
-  auto frag = [&](const unsigned char* tile, int row, int kk) -> typename MF::frag {
+  auto frag = [&](const unsigned char* tile, int row, int kk) __attribute__((always_inline)) -> typename MF::frag {
     if constexpr (MF::KW == 8) {
       const int chunk = 2 * kk + hh;
       return *reinterpret_cast<const bf16x8*>(tile + row * ROWB + ((chunk ^ lds_swizzle(row)) << 4));
@@ -159,7 +176,7 @@ __device__ __forceinline__ void gemm_mainloop(const T* __restrict__ A, const T* 
       return *reinterpret_cast<const float*>(tile + row * ROWB + (((e >> 2) ^ lds_swizzle(row)) << 4) + ((e & 3) << 2));
     }
   };
-  auto compute = [&](int kt) {
+  auto compute = [&](int kt) __attribute__((always_inline)) {
     const unsigned char* ta = ring_a + (kt % SA) * Cfg::A_STAGE;
     const unsigned char* tb = ring_w + (kt % SW) * Cfg::W_STAGE;
     if constexpr (Cfg::KSPLIT) {
@@ -177,25 +194,36 @@ __device__ __forceinline__ void gemm_mainloop(const T* __restrict__ A, const T* 
 #pragma unroll
           for (int j = 0; j < TN; ++j) acc[i][j] = MF::mma(af[i], bfr[j], acc[i][j]);
       }
-    } else {
-      // all of a stage's fragments are read before its MFMAs issue, so the LDS latency of later
-      // k-steps hides behind the MFMAs of earlier ones
-      const int wm = wu / Cfg::WN, wn = wu % Cfg::WN;
-      typename MF::frag af[KPS][TM], bfr[KPS][TN];
-#pragma unroll
-      for (int kk = 0; kk < KPS; ++kk) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i) af[kk][i] = frag(ta, (wm * TM + i) * 32 + r, kk);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) bfr[kk][j] = frag(tb, (wn * TN + j) * 32 + r, kk);
-      }
-#pragma unroll
-      for (int kk = 0; kk < KPS; ++kk)
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j) acc[i][j] = MF::mma(af[kk][i], bfr[kk][j], acc[i][j]);
     }
+  };
+  // Plain layout, software-pipelined over parts of KPP k-steps: the fragment reads of part q are
+  // issued before the MFMAs of part q-1, which do not depend on them, so those MFMAs cover the
+  // LDS latency.  A part holds about 8 MFMAs; two register buffers alternate.
+  constexpr int KPP_W = ORTHRUS_PART_MFMAS / (TM * TN) < 1 ? 1 : ORTHRUS_PART_MFMAS / (TM * TN);
+  constexpr int KPP = Cfg::KSPLIT ? 1 : (KPP_W > KPS ? KPS : KPP_W);
+  constexpr int NP = KPS / KPP;  // parts per stage
+  static_assert(KPS % KPP == 0, "parts tile a stage");
+  constexpr int FA = KPP * TM, FB = KPP * TN;
+  using Frag = typename MF::frag;
+  const int wm = wu / Cfg::WN, wn = wu % Cfg::WN;
+  auto read_part = [&](int kt, int p, Frag (&af)[FA], Frag (&bfr)[FB]) __attribute__((always_inline)) {
+    const unsigned char* ta = ring_a + (kt % SA) * Cfg::A_STAGE;
+    const unsigned char* tb = ring_w + (kt % SW) * Cfg::W_STAGE;
+#pragma unroll
+    for (int k = 0; k < KPP; ++k) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[k * TM + i] = frag(ta, (wm * TM + i) * 32 + r, p * KPP + k);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bfr[k * TN + j] = frag(tb, (wn * TN + j) * 32 + r, p * KPP + k);
+    }
+  };
+  auto mma_part = [&](const Frag (&af)[FA], const Frag (&bfr)[FB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < KPP; ++k)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = MF::mma(af[k * TM + i], bfr[k * TN + j], acc[i][j]);
   };
 
   const int nk = K / BK;
@@ -204,12 +232,15 @@ __device__ __forceinline__ void gemm_mainloop(const T* __restrict__ A, const T* 
   } else {
     for (int s = 0; s < SA - 1 && s < nk; ++s) issue_a(s);
   }
-  for (int kt = 0; kt < nk; ++kt) {
+  // Make stage kt visible to every wave and refill the ring slot of stage kt-1.
+  auto sync_stage = [&](int kt) __attribute__((always_inline)) {
     // this wave's share of stage kt has landed once only its younger stages are outstanding
     if (w_role) wait_stages<SW, NLW>(min(SW - 2, nk - 1 - kt));
     else wait_stages<SA, NLA>(min(SA - 2, nk - 1 - kt));
-    // Both tiles of stage kt are in LDS and stage kt-1 is fully consumed.  A bare s_barrier:
-    // __syncthreads() would add a fence that waits for every outstanding load.
+    // This wave's LDS reads of stage kt-1 are complete, so after the barrier its slot may be
+    // overwritten.  A bare s_barrier: __syncthreads() would add a fence that waits for every
+    // outstanding load.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (w_role) {
@@ -217,7 +248,40 @@ __device__ __forceinline__ void gemm_mainloop(const T* __restrict__ A, const T* 
     } else {
       if (kt + SA - 1 < nk) issue_a(kt + SA - 1);
     }
-    compute(kt);
+  };
+  if constexpr (Cfg::KSPLIT) {
+    for (int kt = 0; kt < nk; ++kt) {
+      sync_stage(kt);
+      compute(kt);
+    }
+  } else {
+    // Part q = NP*kt + p goes to buffer q % 2.  The loop runs two stages per trip so that the
+    // buffer of every part is a compile-time choice whatever NP is.
+    Frag fa[2][FA], fb[2][FB];
+    auto run_stage = [&](int kt, int par) __attribute__((always_inline)) {
+      sync_stage(kt);
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int cur = (par * NP + p) & 1;
+        read_part(kt, p, fa[cur], fb[cur]);
+        // keep the scheduler from hoisting the independent MFMAs above the reads, which would
+        // leave the next part's MFMAs waiting on them again
+        __builtin_amdgcn_sched_barrier(0);
+        if (p > 0 || kt > 0) mma_part(fa[cur ^ 1], fb[cur ^ 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      run_stage(kt, 0);
+      run_stage(kt + 1, 1);
+    }
+    if (kt < nk) {
+      run_stage(kt, 0);
+      mma_part(fa[(NP - 1) & 1], fb[(NP - 1) & 1]);
+    } else {
+      mma_part(fa[(2 * NP - 1) & 1], fb[(2 * NP - 1) & 1]);
+    }
   }
 
   if constexpr (Cfg::KSPLIT) {

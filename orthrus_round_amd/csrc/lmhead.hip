@@ -32,7 +32,7 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
 }
 
 template <typename T, typename Cfg>
-__global__ __launch_bounds__(256) void lmhead_kernel(LmArgs a) {
+__global__ __launch_bounds__(256) ORTHRUS_GEMM_WAVES void lmhead_kernel(LmArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int mtiles = (a.M + Cfg::BM - 1) / Cfg::BM;
   int sp, mt, nt;
