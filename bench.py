@@ -31,6 +31,8 @@ def parse():
     p.add_argument("--layers", type=int, default=8)
     p.add_argument("--precision", default="bf16", choices=["bf16", "fp32"])
     p.add_argument("--kv-chunk", type=int, default=640)
+    p.add_argument("--attn-chunk", type=int, default=1536,
+                   help="kv_chunk of the batched attention measurement (16 ragged sequences up to 16K keys)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-attn", action="store_true")
     p.add_argument("--no-extras", action="store_true", help="skip the block sweep and trajectory match")
@@ -186,7 +188,7 @@ def attention_roofline(kv_chunk):
                      "frac": round(byts / ms / 1e6 / HBM_PEAK_GBS, 4)}
     return {"workload": "batch 16, 32Q/8KV, D128, ctx U[512,16384], 16-token paged random order, bf16->fp32, "
                         "cold (512 MiB read before each launch)",
-            "sum_ctx": n_sum, **res}
+            "sum_ctx": n_sum, "kv_chunk": kv_chunk, **res}
 
 
 def cpu_baseline(W, shape, prompts_np, tokens_per_round_seq, kv_seed=9):
@@ -351,7 +353,7 @@ def main():
     if not args.no_extras:
         sweep = block_sweep(dec, prompts)
         match = trajectory_match(dec, W, shape, prompts, args.match_tokens, args.kv_chunk)
-    attn = None if args.no_attn else attention_roofline(1024)
+    attn = None if args.no_attn else attention_roofline(args.attn_chunk)
     calibration_copy()
     tokens_per_round_seq = committed / (args.steps * args.batch)
     cpu = None

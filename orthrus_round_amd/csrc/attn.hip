@@ -114,9 +114,15 @@ struct AttnTile {
   static_assert(STAGES >= 2, "ring needs two stages");
   static_assert(NI >= 1 && NI * NT == 32 * CPR, "tile must split evenly over the workgroup");
   static constexpr size_t LDS_BYTES = (size_t)STAGES * STAGE_BYTES;
-  // K and V rows are stored with their 16-byte chunks XOR-swizzled so that 32 lanes reading the
-  // same chunk of 32 different rows hit distinct LDS banks.
-  __host__ __device__ static constexpr int swz(int row) { return CPR >= 16 ? (row & 15) : ((row >> 1) & 7); }
+  // K and V rows are stored with their 16-byte chunks XOR-swizzled against LDS bank conflicts.
+  // Two read patterns must be conflict-free: the K fragment reads (16 consecutive rows, the
+  // same chunk) and the transposed V reads (4 consecutive keys 4e..4e+3 times chunks 4c..4c+3).
+  // For 16-chunk rows the XOR mask is linear in the row's low four bits, bits 0..3 mapping to
+  // masks 4, 10, 1, 2: a bijection on 16 rows (first pattern), and keys differing in bits 0-1
+  // land in different groups of four chunks (second pattern).
+  __host__ __device__ static constexpr int swz(int row) {
+    return CPR >= 16 ? (((row & 1) << 2) ^ (((row >> 1) & 1) * 10) ^ ((row >> 2) & 3)) : ((row >> 1) & 7);
+  }
 };
 
 // Softmax bookkeeping is in log2 units.  A row's reference maximum m is only raised when a tile
@@ -308,7 +314,12 @@ __global__ __launch_bounds__(64 * G) void attn_kernel(AttnArgs a) {
         mt = fmaxf(mt, sv[i]);
       }
     }
-    mt = fmaxf(mt, shfl_xor_f(mt, 32)) * csc;  // the row's tile maximum, log2 units (scale > 0)
+    {
+      // the row's tile maximum over both lane halves (a lane swap, not an LDS shuffle), in log2
+      // units (scale > 0)
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+      mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * csc;
+    }
     const bool raise = mt > m_run + kLazy;
     if (__any(raise)) {
       const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
