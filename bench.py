@@ -39,6 +39,8 @@ def parse():
     p.add_argument("--counters", action="store_true",
                    help="hardware-counter mode: prefill, the timed rounds and the calibration copy only")
     p.add_argument("--match-tokens", type=int, default=64)
+    p.add_argument("--control-chunk", type=int, default=1024,
+                   help="kv_chunk of the divergence control runs (another key summation order)")
     return p.parse_args()
 
 
@@ -285,6 +287,73 @@ def trajectory_match(dec, W, shape, prompts, n_tokens, kv_chunk):
     return out
 
 
+def first_divergence(a, b):
+    """Index of the first differing token of two equal-length rows, or None."""
+    d = np.nonzero(np.asarray(a) != np.asarray(b))[0]
+    return int(d[0]) if d.size else None
+
+
+def divergence_control(dec, prompts, n_tokens, kv_chunk, other_chunk):
+    """Greedy trajectories when the attention sums keys in another chunking (another summation
+    order, as a kernel that is not batch-invariant would): the invariant pairing (Orthrus vs AR at
+    one kv_chunk) next to AR vs AR and Orthrus vs AR across two kv_chunks, with the positions at
+    which the trajectories part."""
+    runs = {}
+    for ch in (kv_chunk, other_chunk):
+        dec.set_kv_chunk(ch)
+        runs[("orthrus", ch)], _ = dec.generate(prompts, n_tokens, use_graph=True)
+        runs[("ar", ch)], _ = dec.generate_ar(prompts, n_tokens, use_graph=True)
+    dec.set_kv_chunk(kv_chunk)
+    B = prompts.shape[0]
+
+    def cmp(x, y):
+        div = [first_divergence(runs[x][i, :n_tokens], runs[y][i, :n_tokens]) for i in range(B)]
+        return {"match_rate": sum(d is None for d in div) / B,
+                "first_divergence": sorted(d for d in div if d is not None)}
+    return {f"orthrus_c{kv_chunk}_vs_ar_c{kv_chunk}": cmp(("orthrus", kv_chunk), ("ar", kv_chunk)),
+            f"ar_c{kv_chunk}_vs_ar_c{other_chunk}": cmp(("ar", kv_chunk), ("ar", other_chunk)),
+            f"orthrus_c{kv_chunk}_vs_ar_c{other_chunk}": cmp(("orthrus", kv_chunk), ("ar", other_chunk)),
+            "sequences": B, "tokens": n_tokens}
+
+
+def memory_overhead(W, shape, batch, kv_chunk, contexts=(1024, 2048, 4096), rounds=4):
+    """Device memory of an Orthrus decoder (32-row rounds) against an AR decoder (1-row steps) with
+    caches sized for each context.  Every buffer is allocated up front, so holding a cache for a
+    context costs the same whatever part of it is filled: a 16-token prompt and a few rounds give
+    the peak.  Both decoders load both views' weights, so peak(Orthrus) - peak(AR) is the runtime
+    overhead of the round."""
+    import torch
+    import synth
+    from orthrus_round_amd.decoder import Decoder
+    prompts = torch.from_numpy(synth.prompt_ids(shape, 7, batch, 16))
+    mib = lambda b: round(b / 2**20, 3)
+    res = {}
+    for ctx in contexts:
+        row = {}
+        for mode, block in (("orthrus", 32), ("ar", 1)):
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+            base = torch.cuda.memory_allocated()
+            torch.cuda.reset_peak_memory_stats()
+            d = Decoder(W, shape, precision="bf16", block=block, max_batch=batch, max_ctx=ctx, kv_chunk=kv_chunk)
+            d.prefill(prompts, max_out=32 * rounds)
+            for _ in range(rounds):
+                d.round_greedy() if mode == "orthrus" else d.ar_step()
+            torch.cuda.synchronize()
+            rb = d.runtime_bytes()
+            row[mode] = {"peak_MiB": mib(torch.cuda.max_memory_allocated() - base),
+                         **{k + "_MiB": mib(v) for k, v in rb.items()}}
+            del d
+        row["orthrus_minus_ar_peak_MiB"] = round(row["orthrus"]["peak_MiB"] - row["ar"]["peak_MiB"], 3)
+        res[str(ctx)] = row
+    torch.cuda.empty_cache()
+    s = shape
+    return {"batch": batch, "contexts": res,
+            "block_kv_at_36_layers_batch1_MiB": mib(32 * 36 * s.kv_heads * s.head_dim * 2 * 2),
+            "note": "block K/V is one layer's buffer, reused by every layer; the paged KV cache is the AR cache "
+                    "and grows with the context"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -349,10 +418,12 @@ def main():
     torch.cuda.synchronize()
     ar_ms = (time.perf_counter() - ta) / 20 * 1e3
 
-    sweep = match = None
+    sweep = match = control = memory = None
     if not args.no_extras:
         sweep = block_sweep(dec, prompts)
         match = trajectory_match(dec, W, shape, prompts, args.match_tokens, args.kv_chunk)
+        control = divergence_control(dec, prompts, args.match_tokens, args.kv_chunk, args.control_chunk)
+        memory = memory_overhead(W, shape, args.batch, args.kv_chunk)
     attn = None if args.no_attn else attention_roofline(args.attn_chunk)
     calibration_copy()
     tokens_per_round_seq = committed / (args.steps * args.batch)
@@ -391,6 +462,8 @@ def main():
         "attention_roofline": attn,
         "round_ms_by_block": sweep,
         "trajectory_match_vs_ar": match,
+        "divergence_control_bf16": control,
+        "memory_vs_ar": memory,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -140,11 +140,15 @@ class Decoder:
                            self.kv_chunk, self.dt, self.dt, 1.0 / float(np.sqrt(s.head_dim)))
 
     def _ws(self, desc):
-        key = (desc.batch, desc.block)
-        if key not in self.attn_ws:
-            self.attn_ws[key] = torch.empty(max(16, L.attn_workspace_bytes(desc)), dtype=torch.uint8,
-                                            device=self.dev)
-        return self.attn_ws[key]
+        """One attention workspace for every call: its size depends on the batch and the chunk count
+        of max_ctx only (not on the block), and is largest at the full batch."""
+        need = max(16, L.attn_workspace_bytes(desc))
+        ws = self.attn_ws.get("chunk_partials")
+        if ws is None or ws.numel() < need:
+            full = max(16, L.attn_workspace_bytes(self._attn_desc(self.B, self.block_alloc)))
+            ws = torch.empty(max(need, full), dtype=torch.uint8, device=self.dev)
+            self.attn_ws["chunk_partials"] = ws
+        return ws
 
     def _layers(self, view: str, nb: int, kb: int, ctx, draft: bool):
         """Decoder layers over nb*kb rows in self.x (in place); K/V to the cache unless draft."""
@@ -188,6 +192,50 @@ class Decoder:
         self.K = block
         self._logits = None
         self.graph = None
+
+    def set_kv_chunk(self, kv_chunk: int):
+        """Use attention key chunks of `kv_chunk` keys.  The chunk fixes the order in which a row's
+        keys are summed, so runs compared bit for bit must use the same value; workspaces and graphs
+        built for another chunk are dropped."""
+        assert kv_chunk > 0 and kv_chunk % 32 == 0
+        self.kv_chunk = kv_chunk
+        self.attn_ws = {}
+        self.graph = None
+
+    def runtime_bytes(self) -> dict:
+        """Device bytes held by this decoder, by kind: the two views' weights, the shared weights,
+        the paged KV cache, the diffusion view's block K/V buffer, the attention workspaces, and every
+        other buffer (activations of a round's rows, LM-head workspace, round state)."""
+        def nb(t):
+            return t.numel() * t.element_size()
+        view = {"ar": 0, "diff": 0}
+        shared = nb(self.embed) + nb(self.lm_head) + nb(self.final_norm)
+        for ly in self.layers:
+            view["ar"] += nb(ly["qkv_ar"]) + nb(ly["o_ar"])
+            view["diff"] += nb(ly["qkv_diff"]) + nb(ly["o_diff"])
+            shared += nb(ly["attn_norm"]) + nb(ly["mlp_norm"]) + nb(ly["gate_up"]) + nb(ly["down"])
+        kv = sum(nb(t) for t in self.k_pages) + sum(nb(t) for t in self.v_pages)
+        blk = nb(self.k_blk) + nb(self.v_blk)
+        attn_ws = sum(nb(t) for t in self.attn_ws.values())
+
+        def tensors(o):
+            if isinstance(o, torch.Tensor):
+                yield o
+            elif isinstance(o, (list, tuple)):
+                for x in o:
+                    yield from tensors(x)
+            elif isinstance(o, dict):
+                for x in o.values():
+                    yield from tensors(x)
+        seen, total = set(), 0
+        for t in tensors(list(vars(self).values())):
+            key = (t.untyped_storage().data_ptr(), t.device)
+            if t.device.type == self.dev.type and key not in seen:
+                seen.add(key)
+                total += t.untyped_storage().nbytes()
+        named = view["ar"] + view["diff"] + shared + kv + blk + attn_ws
+        return {"weights_ar_view": view["ar"], "weights_diff_view": view["diff"], "weights_shared": shared,
+                "kv_cache": kv, "block_kv": blk, "attn_workspace": attn_ws, "other_buffers": total - named}
 
     def prefill(self, prompts: torch.Tensor, max_out: int):
         """AR prefill of prompts[:, :-1] in causal chunks of the allocated block; anchor :=

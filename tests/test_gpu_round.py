@@ -47,6 +47,24 @@ def test_tiny_fp32_trajectory_and_accepts_match_oracle(tiny, prompts):
     print(f"rounds {st.rounds} tpf {st.tpf:.3f}")
 
 
+def test_other_kv_chunk_matches_oracle_and_accounts_memory(tiny, prompts):
+    """Another attention key chunking (another summation order) still reproduces the oracle's
+    trajectory and accepts in fp32; the decoder's memory accounting covers the block K/V buffer
+    (one layer's block rows, reused by every layer) and the paged cache of every layer."""
+    W, Wt = tiny
+    dec = make(W)
+    dec.set_kv_chunk(64)
+    toks, st = dec.generate(prompts[:1], 96, poll_every=1, record_accepts=True)
+    ref = Dc.generate(Wt, prompts[0], 96)
+    assert list(toks[0]) == ref.tokens
+    assert [int(h[0]) for h in st.accept_hist[: len(ref.rounds)]] == [r.accept for r in ref.rounds]
+    rb = dec.runtime_bytes()
+    s = SHAPE
+    assert rb["block_kv"] == 2 * 1 * 32 * s.kv_heads * s.head_dim * 4
+    assert rb["kv_cache"] == 2 * s.layers * dec.num_pages * s.kv_heads * dec.page * s.head_dim * 4
+    assert rb["weights_diff_view"] == rb["weights_ar_view"] > 0
+
+
 @pytest.mark.parametrize("block", [8, 1])
 def test_smaller_block_matches_oracle(tiny, prompts, block):
     """A decoder built for 32-row rounds, switched to `block` rows: tokens and per-round accepts
