@@ -10,7 +10,7 @@ namespace orthrus {
 namespace {
 
 template <typename T, typename OutT, typename Cfg, int EPI>
-__global__ __launch_bounds__(256) ORTHRUS_GEMM_WAVES void gemm_kernel(const T* __restrict__ A, const T* __restrict__ W,
+__global__ __launch_bounds__(Cfg::NT) ORTHRUS_GEMM_WAVES void gemm_kernel(const T* __restrict__ A, const T* __restrict__ W,
                                                    const OutT* residual, OutT* C, int M, int N, int K) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int mtiles = (M + Cfg::BM - 1) / Cfg::BM;
@@ -23,7 +23,7 @@ __global__ __launch_bounds__(256) ORTHRUS_GEMM_WAVES void gemm_kernel(const T* _
   gemm_mainloop<T, Cfg>(A, W, M, N, K, m0, n0, smem, acc);
   constexpr int NBI = Cfg::BM / 32, NBJ = Cfg::BN / 32;
   if constexpr (!Cfg::KSPLIT) park_plain<Cfg>(smem, acc);
-  // the tile's 32x32 blocks are now in LDS (k-split: four partials each); wave q % 4 stores block q
+  // the tile's 32x32 blocks are now in LDS (k-split: four partials each); wave q % NW stores block q
   auto block = [&](int i, int j) -> f32x16 {
     if constexpr (Cfg::KSPLIT) return ks4_sum<Cfg>(smem, i, j);
     else return plain_block<Cfg>(smem, i, j);
@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) ORTHRUS_GEMM_WAVES void gemm_kernel(const T* _
     for (int i = 0; i < NBI; ++i)
 #pragma unroll
       for (int j = 0; j < NBJ; j += 2) {
-        if ((i * (NBJ / 2) + j / 2) % 4 != wu) continue;
+        if ((i * (NBJ / 2) + j / 2) % Cfg::NW != wu) continue;
         const int ng = n0 + j * 32;  // multiple of 64
         if (ng >= N) continue;
         const f32x16 g = block(i, j), u = block(i, j + 1);
@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256) ORTHRUS_GEMM_WAVES void gemm_kernel(const T* _
     for (int i = 0; i < NBI; ++i)
 #pragma unroll
       for (int j = 0; j < NBJ; ++j) {
-        if ((i * NBJ + j) % 4 != wu) continue;
+        if ((i * NBJ + j) % Cfg::NW != wu) continue;
         const int n = n0 + j * 32 + r;
         if (n >= N) continue;
         const f32x16 v = block(i, j);
@@ -91,8 +91,11 @@ template <typename T> using KsBig = KsCfg<T, 64, 64, ORTHRUS_KSB_RINGS>;
 template <typename T> using PlainSmall = GemmCfg<T, 32, 128, 1, 4, 4, 4>;
 template <typename T> using PlainMid = GemmCfg<T, 64, 128, 2, 2, 3, 3>;
 template <typename T> using PlainBig = GemmCfg<T, 128, 128, 2, 2, ORTHRUS_PB_RINGS>;
-#ifndef ORTHRUS_WIDE_BIG_CFG
-#define ORTHRUS_WIDE_BIG_CFG(T) PlainBig<T>
+// 256-row tiles (a whole M = 256 round in one tile, so each weight tile is streamed once) run
+// eight wavefronts of 64x64: with one workgroup per CU that is still two wavefronts per SIMD.
+// The weight ring is the deeper one: it streams from HBM, the activation ring from L2.
+#ifndef ORTHRUS_WIDE_HUGE_CFG
+#define ORTHRUS_WIDE_HUGE_CFG(T) GemmCfg<T, 256, 128, 4, 2, 2, 4>
 #endif
 constexpr int kWideN = 16384;
 
@@ -109,16 +112,16 @@ int32_t launch_cfg(int M, int N, int K, int epi, const void* a, const void* w, c
   switch (epi) {
     case ORTHRUS_EPI_STORE:
       allow_lds(gemm_kernel<T, OutT, Cfg, ORTHRUS_EPI_STORE>, lds);
-      hipLaunchKernelGGL((gemm_kernel<T, OutT, Cfg, ORTHRUS_EPI_STORE>), grid, dim3(256), lds, st, A, Wt, R, C, M, N, K);
+      hipLaunchKernelGGL((gemm_kernel<T, OutT, Cfg, ORTHRUS_EPI_STORE>), grid, dim3(Cfg::NT), lds, st, A, Wt, R, C, M, N, K);
       break;
     case ORTHRUS_EPI_RESIDUAL:
       allow_lds(gemm_kernel<T, OutT, Cfg, ORTHRUS_EPI_RESIDUAL>, lds);
-      hipLaunchKernelGGL((gemm_kernel<T, OutT, Cfg, ORTHRUS_EPI_RESIDUAL>), grid, dim3(256), lds, st, A, Wt, R, C, M,
+      hipLaunchKernelGGL((gemm_kernel<T, OutT, Cfg, ORTHRUS_EPI_RESIDUAL>), grid, dim3(Cfg::NT), lds, st, A, Wt, R, C, M,
                          N, K);
       break;
     default:
       allow_lds(gemm_kernel<T, OutT, Cfg, ORTHRUS_EPI_SWIGLU>, lds);
-      hipLaunchKernelGGL((gemm_kernel<T, OutT, Cfg, ORTHRUS_EPI_SWIGLU>), grid, dim3(256), lds, st, A, Wt, R, C, M, N,
+      hipLaunchKernelGGL((gemm_kernel<T, OutT, Cfg, ORTHRUS_EPI_SWIGLU>), grid, dim3(Cfg::NT), lds, st, A, Wt, R, C, M, N,
                          K);
       break;
   }
@@ -133,7 +136,8 @@ int32_t launch(int M, int N, int K, int epi, const void* a, const void* w, const
   }
   if (M <= 32) return launch_cfg<T, OutT, PlainSmall<T>>(M, N, K, epi, a, w, res, c, st);
   if (M <= 64) return launch_cfg<T, OutT, PlainMid<T>>(M, N, K, epi, a, w, res, c, st);
-  return launch_cfg<T, OutT, ORTHRUS_WIDE_BIG_CFG(T)>(M, N, K, epi, a, w, res, c, st);
+  if (M <= 128) return launch_cfg<T, OutT, PlainBig<T>>(M, N, K, epi, a, w, res, c, st);
+  return launch_cfg<T, OutT, ORTHRUS_WIDE_HUGE_CFG(T)>(M, N, K, epi, a, w, res, c, st);
 }
 
 template <typename T>

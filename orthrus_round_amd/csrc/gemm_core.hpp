@@ -37,40 +37,43 @@
 
 namespace orthrus {
 
-template <typename T, int BM_, int BN_, int SA_, int SW_>
+template <typename T, int BM_, int BN_, int SA_, int SW_, int NW_>
 struct StageRings {
   static constexpr int BM = BM_, BN = BN_, SA = SA_, SW = SW_;
+  static constexpr int NW = NW_, NT = 64 * NW_;  // wavefronts and threads per workgroup
+  static constexpr int RW = NW_ / 2;             // wavefronts per load role (A or W)
   static constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
   static constexpr int BK = 8 * EPC;          // 128 bytes of k per stage
   static constexpr int ROWB = 128;            // bytes per tile row per stage
   static constexpr int A_STAGE = BM * ROWB, W_STAGE = BN * ROWB;
-  static constexpr int NLA = BM / 16;         // 1 KiB wave loads per A-wave per stage (2 A-waves)
-  static constexpr int NLW = BN / 16;         // per W-wave per stage (2 W-waves)
-  static_assert(NLA * 16 == BM && NLW * 16 == BN && NLA >= 1 && NLW >= 1, "tile rows must split over 2 waves");
+  static constexpr int NLA = BM / (8 * RW);   // 1 KiB wave loads per A-wave per stage
+  static constexpr int NLW = BN / (8 * RW);   // per W-wave per stage
+  static_assert(NW == 4 || NW == 8, "four or eight wavefronts per workgroup");
+  static_assert(NLA * 8 * RW == BM && NLW * 8 * RW == BN && NLA >= 1 && NLW >= 1,
+                "tile rows must split over each role's waves");
   static_assert(SA >= 2 && SW >= 2, "rings need two stages");
   static_assert((SA - 2) * NLA < 64 && (SW - 2) * NLW < 64, "loads in flight must fit the vmcnt counter");
   static constexpr size_t RING_BYTES = (size_t)SA * A_STAGE + (size_t)SW * W_STAGE;
 };
 
 template <typename T, int BM_, int BN_, int WM_, int WN_, int SA_, int SW_>
-struct GemmCfg : StageRings<T, BM_, BN_, SA_, SW_> {
+struct GemmCfg : StageRings<T, BM_, BN_, SA_, SW_, WM_ * WN_> {
   static constexpr int WM = WM_, WN = WN_;
   static constexpr bool KSPLIT = false;
-  static_assert(WM * WN == 4, "4 wavefronts per workgroup");
   static constexpr int TM = BM_ / (32 * WM), TN = BN_ / (32 * WN);
   static_assert(TM >= 1 && TN >= 1 && TM * 32 * WM == BM_ && TN * 32 * WN == BN_, "tile shape");
   static constexpr size_t TILE_BYTES = (size_t)BM_ * BN_ * 4;  // the fp32 tile parked for the epilogue
-  static constexpr size_t RING = StageRings<T, BM_, BN_, SA_, SW_>::RING_BYTES;
+  static constexpr size_t RING = StageRings<T, BM_, BN_, SA_, SW_, WM_ * WN_>::RING_BYTES;
   static constexpr size_t LDS_BYTES = RING > TILE_BYTES ? RING : TILE_BYTES;
 };
 
 template <typename T, int BM_, int BN_, int SA_, int SW_>
-struct KsCfg : StageRings<T, BM_, BN_, SA_, SW_> {
+struct KsCfg : StageRings<T, BM_, BN_, SA_, SW_, 4> {
   static constexpr int WM = 1, WN = 1;
   static constexpr bool KSPLIT = true;
   static constexpr int TM = BM_ / 32, TN = BN_ / 32;
   static constexpr size_t PART_BYTES = (size_t)4 * TM * TN * 16 * 64 * 4;  // 4 waves' partial tiles
-  static constexpr size_t RING = StageRings<T, BM_, BN_, SA_, SW_>::RING_BYTES;
+  static constexpr size_t RING = StageRings<T, BM_, BN_, SA_, SW_, 4>::RING_BYTES;
   static constexpr size_t LDS_BYTES = RING > PART_BYTES ? RING : PART_BYTES;
 };
 
@@ -117,16 +120,17 @@ __device__ __forceinline__ void load_to_lds16(const void* src, unsigned char* ds
   __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
 }
 
-// Stage kt of one role's ring: load j of wave wl fills tile rows (2j + wl)*8 .. +7 of slot kt % S.
-// Takes its state by value: lambdas capturing the per-lane pointers by reference were left in
-// scratch memory by the compiler when the two rings differ in depth.
-template <int S, int NL, int STAGE, int BK, typename T>
+// Stage kt of one role's ring: load j of wave wl (of RW role waves) fills tile rows
+// (RW*j + wl)*8 .. +7 of slot kt % S.  Takes its state by value: lambdas capturing the per-lane
+// pointers by reference were left in scratch memory by the compiler when the two rings differ in
+// depth.
+template <int S, int NL, int STAGE, int BK, int RW, typename T>
 __device__ __forceinline__ void issue_stage(const T* src0, int row0, int lim, int K, unsigned char* ring, int kt,
                                             int wl) {
   unsigned char* dst = ring + (kt % S) * STAGE;
 #pragma unroll
   for (int j = 0; j < NL; ++j)
-    load_to_lds16(src0 + (size_t)min(row0 + 16 * j, lim) * K + (size_t)kt * BK, dst + (2 * j + wl) * 8 * 128);
+    load_to_lds16(src0 + (size_t)min(row0 + 8 * RW * j, lim) * K + (size_t)kt * BK, dst + (RW * j + wl) * 8 * 128);
 }
 
 // Shared main loop.  On return acc holds this wave's accumulators: its WM x WN share of the tile
@@ -141,8 +145,9 @@ __device__ __forceinline__ void gemm_mainloop(const T* __restrict__ A, const T* 
   constexpr int KPS = BK / MF::KSTEP;  // k-steps per stage (4 for bf16, 16 for fp32)
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, r = lane & 31;
   const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform wave index
-  const bool w_role = wu >= 2;                                // waves 2-3 load W, 0-1 load A
-  const int wl = wu & 1;                                      // wave within its role
+  constexpr int RW = Cfg::RW;
+  const bool w_role = wu >= RW;                               // the upper half loads W, the lower A
+  const int wl = wu % RW;                                     // wave within its role
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -152,20 +157,21 @@ __device__ __forceinline__ void gemm_mainloop(const T* __restrict__ A, const T* 
   unsigned char* const ring_w = lds + (size_t)SA * Cfg::A_STAGE;
 
   // Per-lane source pointers of this wave's loads (k offset added per stage).  Load j of role wave
-  // wl fills tile rows (2j + wl)*8 .. +7; lane l lands in row +l/8, slot l%8, and fetches the chunk
-  // that slot holds under the swizzle.  Rows past M or N read a clamped valid row: those outputs
-  // are never stored.
-  // Row trow = 16j + 8wl + l/8 has swizzle (trow/2) mod 8 = (4wl + l/16) mod 8 for every j.
+  // wl fills tile rows (RW*j + wl)*8 .. +7; lane l lands in row +l/8, slot l%8, and fetches the
+  // chunk that slot holds under the swizzle.  Rows past M or N read a clamped valid row: those
+  // outputs are never stored.
+  // Row trow = 8RW*j + 8wl + l/8 has swizzle (trow/2) mod 8 = (4wl + l/16) mod 8 for every j
+  // (4RW*j is a multiple of 8).
   // The row offset is recomputed per load: an array of per-load pointers ends up in scratch.
   const T* const mat = w_role ? W : A;
   const int lim = (w_role ? N : M) - 1;
   const int row0 = (w_role ? n0 : m0) + wl * 8 + (lane >> 3);
   const T* const src0 = mat + ((lane & 7) ^ lds_swizzle(wl * 8 + (lane >> 3))) * EPC;
   auto issue_a = [&](int kt) __attribute__((always_inline)) {
-    issue_stage<SA, NLA, Cfg::A_STAGE, BK>(src0, row0, lim, K, ring_a, kt, wl);
+    issue_stage<SA, NLA, Cfg::A_STAGE, BK, RW>(src0, row0, lim, K, ring_a, kt, wl);
   };
   auto issue_w = [&](int kt) __attribute__((always_inline)) {
-    issue_stage<SW, NLW, Cfg::W_STAGE, BK>(src0, row0, lim, K, ring_w, kt, wl);
+    issue_stage<SW, NLW, Cfg::W_STAGE, BK, RW>(src0, row0, lim, K, ring_w, kt, wl);
   };
   auto frag = [&](const unsigned char* tile, int row, int kk) __attribute__((always_inline)) -> typename MF::frag {
     if constexpr (MF::KW == 8) {

@@ -32,7 +32,7 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
 }
 
 template <typename T, typename Cfg>
-__global__ __launch_bounds__(256) ORTHRUS_GEMM_WAVES void lmhead_kernel(LmArgs a) {
+__global__ __launch_bounds__(Cfg::NT) ORTHRUS_GEMM_WAVES void lmhead_kernel(LmArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int mtiles = (a.M + Cfg::BM - 1) / Cfg::BM;
   int sp, mt, nt;
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) ORTHRUS_GEMM_WAVES void lmhead_kernel(LmArgs a
     }
   }
   __syncthreads();
-  for (int mrow = threadIdx.x; mrow < Cfg::BM; mrow += 256) {
+  for (int mrow = threadIdx.x; mrow < Cfg::BM; mrow += Cfg::NT) {
     const int m = m0 + mrow;
     if (m >= a.M) continue;
     uint64_t best = red_best[mrow * Cfg::WN];
@@ -149,13 +149,17 @@ int32_t launch(LmArgs& a, hipStream_t st) {
   const int mtiles = (a.M + Cfg::BM - 1) / Cfg::BM;
   const size_t lds = std::max(Cfg::LDS_BYTES, (size_t)Cfg::BM * Cfg::WN * 16);
   allow_lds(lmhead_kernel<T, Cfg>, lds);
-  hipLaunchKernelGGL((lmhead_kernel<T, Cfg>), dim3(mtiles * a.ntiles), dim3(256), lds, st, a);
+  hipLaunchKernelGGL((lmhead_kernel<T, Cfg>), dim3(mtiles * a.ntiles), dim3(Cfg::NT), lds, st, a);
   return check_launch("orthrus_lmhead_argmax");
 }
 
 constexpr int kLmBN = 128;
 #ifndef ORTHRUS_LM_BIG_CFG
 #define ORTHRUS_LM_BIG_CFG(T) GemmCfg<T, 128, kLmBN, 2, 2, 3, 2>
+#endif
+// above 128 rows: 256-row tiles of eight wavefronts (each weight tile streamed once per 256 rows)
+#ifndef ORTHRUS_LM_HUGE_CFG
+#define ORTHRUS_LM_HUGE_CFG(T) GemmCfg<T, 256, kLmBN, 4, 2, 2, 4>
 #endif
 
 }  // namespace
@@ -201,11 +205,13 @@ extern "C" int32_t orthrus_lmhead_argmax(const orthrus_lmhead_desc_t* d, const v
   if (d->dtype == ORTHRUS_BF16) {
     if (a.M <= 32) s = launch<bf16, GemmCfg<bf16, 32, kLmBN, 1, 4, 4, 4>>(a, st);
     else if (a.M <= 64) s = launch<bf16, GemmCfg<bf16, 64, kLmBN, 2, 2, 3, 3>>(a, st);
-    else s = launch<bf16, ORTHRUS_LM_BIG_CFG(bf16)>(a, st);
+    else if (a.M <= 128) s = launch<bf16, ORTHRUS_LM_BIG_CFG(bf16)>(a, st);
+    else s = launch<bf16, ORTHRUS_LM_HUGE_CFG(bf16)>(a, st);
   } else {
     if (a.M <= 32) s = launch<float, GemmCfg<float, 32, kLmBN, 1, 4, 4, 4>>(a, st);
     else if (a.M <= 64) s = launch<float, GemmCfg<float, 64, kLmBN, 2, 2, 3, 3>>(a, st);
-    else s = launch<float, ORTHRUS_LM_BIG_CFG(float)>(a, st);
+    else if (a.M <= 128) s = launch<float, ORTHRUS_LM_BIG_CFG(float)>(a, st);
+    else s = launch<float, ORTHRUS_LM_HUGE_CFG(float)>(a, st);
   }
   if (s != ORTHRUS_OK) return s;
   hipLaunchKernelGGL(lmhead_finalize, dim3(a.M), dim3(64), 0, st, a.part_best, a.part_m, a.part_s, a.ntiles, token_out,
