@@ -305,15 +305,40 @@ def divergence_control(dec, prompts, n_tokens, kv_chunk, other_chunk):
         runs[("ar", ch)], _ = dec.generate_ar(prompts, n_tokens, use_graph=True)
     dec.set_kv_chunk(kv_chunk)
     B = prompts.shape[0]
+    margins = ar_margins(dec, prompts, n_tokens)
+    ref = runs[("ar", kv_chunk)]
+    assert np.array_equal(margins["tokens"], ref[:, :n_tokens]), "eager AR with logits differs from the graph run"
+    gap = margins["top2_gap"]
 
     def cmp(x, y):
         div = [first_divergence(runs[x][i, :n_tokens], runs[y][i, :n_tokens]) for i in range(B)]
+        at = [(d, float(gap[i, d])) for i, d in enumerate(div) if d is not None]
         return {"match_rate": sum(d is None for d in div) / B,
-                "first_divergence": sorted(d for d in div if d is not None)}
+                "first_divergence": sorted(d for d, _ in at),
+                "ar_top2_gap_at_divergence": [round(g, 6) for _, g in sorted(at)],
+                "gap_percentile_at_divergence": [round(float((gap < g).mean()) * 100, 1) for _, g in sorted(at)]}
     return {f"orthrus_c{kv_chunk}_vs_ar_c{kv_chunk}": cmp(("orthrus", kv_chunk), ("ar", kv_chunk)),
             f"ar_c{kv_chunk}_vs_ar_c{other_chunk}": cmp(("ar", kv_chunk), ("ar", other_chunk)),
             f"orthrus_c{kv_chunk}_vs_ar_c{other_chunk}": cmp(("orthrus", kv_chunk), ("ar", other_chunk)),
+            "ar_top2_gap_median": round(float(np.median(gap)), 6),
+            "ar_top2_gap_min": round(float(gap.min()), 6),
             "sequences": B, "tokens": n_tokens}
+
+
+def ar_margins(dec, prompts, n_tokens):
+    """Greedy AR steps (eager) that also keep the logits: per sequence and step, the gap between the
+    largest and the second-largest logit of the reference AR model (its decisiveness there)."""
+    import torch
+    B, V = prompts.shape[0], dec.shape.vocab
+    dec.prefill(torch.as_tensor(prompts), n_tokens)
+    buf = torch.empty((dec.B, V), dtype=torch.float32, device=dec.dev)
+    gaps = np.zeros((B, n_tokens))
+    for t in range(n_tokens):
+        dec.ar_step(0.0, 0, logits=buf)
+        top = torch.topk(buf[:B], 2, dim=1).values
+        gaps[:, t] = (top[:, 0] - top[:, 1]).cpu().numpy()
+    torch.cuda.synchronize()
+    return {"tokens": dec.out_tokens.cpu().numpy()[:B, :n_tokens], "top2_gap": gaps}
 
 
 def memory_overhead(W, shape, batch, kv_chunk, contexts=(1024, 2048, 4096), rounds=4):

@@ -288,14 +288,15 @@ class Decoder:
                            self._lse[0], self._lse[1], self.draft, self.ctx_len, self.anchor, self.accept,
                            self.out_tokens, self.out_len, self.round, self.done, self.max_out, self.max_ctx)
 
-    def ar_step(self, temperature: float = 0.0, seed: int = 0):
-        """One plain AR step for every sequence: a one-row causal pass, argmax/sample, commit."""
+    def ar_step(self, temperature: float = 0.0, seed: int = 0, logits: torch.Tensor | None = None):
+        """One plain AR step for every sequence: a one-row causal pass, argmax/sample, commit.
+        With `logits` (fp32 [batch, vocab]) the step also writes the LM head's logits there."""
         B, s = self.B, self.shape
         L.embed_block(B, 1, s.hidden, self.dt, self.embed, self.anchor, None, 0, 0, s.mask_id, self.x)
         self._layers("ar", B, 1, self.ctx_len, draft=False)
         tok = self.target[:, :1]
         t_flat = self.target.view(-1)[:B]
-        self._lm_head(B, 1, t_flat, temperature, seed, L.STREAM_AR)
+        self._lm_head(B, 1, t_flat, temperature, seed, L.STREAM_AR, logits=logits)
         L.consensus_commit(B, 1, t_flat, t_flat, self.ctx_len, self.anchor, self.accept, self.out_tokens,
                            self.out_len, self.round, self.done, self.max_out, self.max_ctx)
         return tok
