@@ -1,0 +1,83 @@
+"""GPU parity at the full-size round configuration: 8 decoder layers at Qwen3-8B width (hidden 4096,
+32Q/8KV heads x 128, SwiGLU 12288, vocabulary 151936), batch 8, the weights of the timed round.
+
+The prompts are 64 tokens so that the oracle (float64, BLAS over rows) finishes in seconds; the
+kernels and their launch configuration are those of the timed round (256-row GEMMs, 151936-wide LM
+head, paged attention with the same kv_chunk).
+
+* Sequence 0's first round through the fp32 decoder (the same bf16-valued weights held in fp32)
+  against the oracle: the 32 draft ids and the 32 verify ids, where an id may differ only at an
+  oracle near-tie (top two logits within 1e-4 relative); the verify pass is run by the oracle on
+  the GPU's own drafts, since an ambiguous draft changes the verify inputs; then the accept count
+  and the new KV length, which are integer logic on the GPU's own ids and must be exact.
+* All 8 sequences: GPU Orthrus == GPU AR over 16 tokens, in fp32 and in bf16 (losslessness).
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from orthrus_round_amd.decoder import Decoder
+from oracle import decode as Dc
+from oracle import model as M
+
+pytestmark = pytest.mark.gpu
+SHAPE = synth.QWEN3_8B_L8
+P = 64
+KV_CHUNK = 640
+
+
+@pytest.fixture(scope="module")
+def weights():
+    return synth.model_weights(SHAPE, cfg=5, diff_std=0.002, bf16=True)
+
+
+@pytest.fixture(scope="module")
+def prompts():
+    return synth.prompt_ids(SHAPE, 5, 8, P)
+
+
+def tie_ok(z, got, ref):
+    """Same id, or an oracle near-tie between the two ids."""
+    if int(got) == int(ref):
+        return True
+    return z[ref] - z[got] <= 1e-4 * max(1.0, abs(z[ref]))
+
+
+def test_first_round_matches_oracle(weights, prompts):
+    dec = Decoder(weights, SHAPE, precision="fp32", block=32, max_batch=8, max_ctx=P + 96, kv_chunk=KV_CHUNK)
+    dec.prefill(torch.from_numpy(prompts), max_out=64)
+    n0 = int(dec.ctx_len[0])
+    dec.round_greedy()
+    torch.cuda.synchronize()
+    d_gpu = dec.draft[0].cpu().numpy().copy()
+    t_gpu = dec.target[0].cpu().numpy().copy()
+    acc_gpu, n_gpu = int(dec.accept[0]), int(dec.ctx_len[0])
+    del dec
+    torch.cuda.empty_cache()
+
+    Wt = M.Weights(weights, SHAPE)
+    cache, anchor = Dc.prefill(Wt, prompts[0], P + 96, rowwise=False)
+    assert cache.n == n0 == P - 1
+    zd = Dc.draft_pass(Wt, cache, [anchor] + [SHAPE.mask_id] * 31, rowwise=False)
+    d_ref = M.argmax_lowest(zd)
+    bad = [i for i in range(32) if not tie_ok(zd[i], d_gpu[i], d_ref[i])]
+    assert not bad, ("drafts", bad, d_gpu[bad], d_ref[bad])
+    zt = Dc.ar_pass(Wt, cache, [anchor] + [int(x) for x in d_gpu[:31]], rowwise=False)
+    t_ref = M.argmax_lowest(zt)
+    bad = [i for i in range(32) if not tie_ok(zt[i], t_gpu[i], t_ref[i])]
+    assert not bad, ("targets", bad, t_gpu[bad], t_ref[bad])
+    k, emitted = Dc.consensus(d_gpu, t_gpu)
+    assert acc_gpu == k
+    assert n_gpu == n0 + min(k + 1, 32)
+    print(f"drafts equal {int((d_gpu == d_ref).sum())}/32, targets equal {int((t_gpu == t_ref).sum())}/32, "
+          f"accept {k}")
+
+
+@pytest.mark.parametrize("precision", ["fp32", "bf16"])
+def test_orthrus_equals_ar_full_width(weights, prompts, precision):
+    dec = Decoder(weights, SHAPE, precision=precision, block=32, max_batch=8, max_ctx=P + 96, kv_chunk=KV_CHUNK)
+    a, st = dec.generate(prompts, 16, use_graph=True)
+    b, _ = dec.generate_ar(prompts, 16, use_graph=True)
+    assert np.array_equal(a[:, :16], b[:, :16]), [int(np.argmax(a[i, :16] != b[i, :16])) for i in range(8)]
+    print(f"{precision}: {st.rounds} rounds for 16 tokens x 8 sequences")
