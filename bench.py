@@ -74,6 +74,33 @@ def event_time_ms(fn, iters=12):
     return float(np.median(times[2:]))
 
 
+def layer_sweep_ms(fn, n_layers, sweeps=4):
+    """Average duration of one launch of `fn(layer)` over back-to-back launches that walk every
+    layer's weights and caches in turn (as the round does).  One sweep over the layers is captured
+    in a HIP graph, so the launches follow each other on the GPU without host gaps, and the replays
+    are timed with one pair of HIP events on the current stream.  The layers' operands together
+    exceed the 256 MiB infinity cache, so each launch streams its own from HBM."""
+    import torch
+    for i in range(n_layers):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n_layers):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    flush_caches()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(sweeps):
+        g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    del g
+    return s.elapsed_time(e) / (sweeps * n_layers)
+
+
 def kernel_table(dec, ctx_np):
     """Per-launch HIP-event times of each kernel class of the round at its in-round shapes."""
     import orthrus_round_amd._lib as L
@@ -82,39 +109,40 @@ def kernel_table(dec, ctx_np):
     H, D, Hq, Hkv, I, V = s.hidden, s.head_dim, s.q_heads, s.kv_heads, s.inter, s.vocab
     dt = dec.dt
     esz = 2 if dt == L.BF16 else 4
-    Wl = dec.layers[0]
+    Ly = dec.layers
+    nl = len(Ly)
     desc = dec._attn_desc(B, K)
     ws = dec._ws(desc)
     n_sum = int(ctx_np.sum())
     tab = {}
 
     def add(name, fn, per_round, bytes_, flops):
-        ms = event_time_ms(fn)
+        ms = layer_sweep_ms(fn, nl)
         tab[name] = dict(ms=ms, per_round=per_round, bytes=bytes_, flops=flops)
 
-    add("gemm_qkv", lambda: L.gemm(M, dec.nqkv, H, dt, dt, L.EPI_STORE, dec.a, Wl["qkv_ar"], None, dec.qkv, dec.gemm_ws),
+    add("gemm_qkv", lambda i: L.gemm(M, dec.nqkv, H, dt, dt, L.EPI_STORE, dec.a, Ly[i]["qkv_ar"], None, dec.qkv, dec.gemm_ws),
         2 * s.layers, (dec.nqkv * H + M * H + M * dec.nqkv) * esz, 2 * M * dec.nqkv * H)
-    add("gemm_o_residual", lambda: L.gemm(M, H, Hq * D, dt, dt, L.EPI_RESIDUAL, dec.o, Wl["o_ar"], dec.x, dec.x, dec.gemm_ws),
+    add("gemm_o_residual", lambda i: L.gemm(M, H, Hq * D, dt, dt, L.EPI_RESIDUAL, dec.o, Ly[i]["o_ar"], dec.x, dec.x, dec.gemm_ws),
         2 * s.layers, (H * Hq * D + M * Hq * D + 2 * M * H) * esz, 2 * M * H * Hq * D)
-    add("gemm_gate_up_swiglu", lambda: L.gemm(M, 2 * I, H, dt, dt, L.EPI_SWIGLU, dec.a, Wl["gate_up"], None, dec.h, dec.gemm_ws),
+    add("gemm_gate_up_swiglu", lambda i: L.gemm(M, 2 * I, H, dt, dt, L.EPI_SWIGLU, dec.a, Ly[i]["gate_up"], None, dec.h, dec.gemm_ws),
         2 * s.layers, (2 * I * H + M * H + M * I) * esz, 2 * M * 2 * I * H)
-    add("gemm_down_residual", lambda: L.gemm(M, H, I, dt, dt, L.EPI_RESIDUAL, dec.h, Wl["down"], dec.x, dec.x, dec.gemm_ws),
+    add("gemm_down_residual", lambda i: L.gemm(M, H, I, dt, dt, L.EPI_RESIDUAL, dec.h, Ly[i]["down"], dec.x, dec.x, dec.gemm_ws),
         2 * s.layers, (H * I + M * I + 2 * M * H) * esz, 2 * M * H * I)
     kv_b = Hkv * D * 2 * esz  # K and V bytes per key
     qo_b = 2 * M * Hq * D * esz
-    add("attn_draft", lambda: L.draft_attn(desc, dec.q, dec.k_pages[0], dec.v_pages[0], dec.page_table, dec.ctx_len,
+    add("attn_draft", lambda i: L.draft_attn(desc, dec.q, dec.k_pages[i], dec.v_pages[i], dec.page_table, dec.ctx_len,
                                            dec.k_blk, dec.v_blk, dec.o, ws),
         s.layers, n_sum * kv_b + M * kv_b + qo_b, 4 * Hq * D * K * (n_sum + B * K))
-    add("attn_verify", lambda: L.verify_attn(desc, dec.q, dec.k_pages[0], dec.v_pages[0], dec.page_table,
+    add("attn_verify", lambda i: L.verify_attn(desc, dec.q, dec.k_pages[i], dec.v_pages[i], dec.page_table,
                                              dec.ctx_len, dec.o, ws),
         s.layers, (n_sum + M) * kv_b + qo_b, 4 * Hq * D * K * (n_sum + B * K))
     d = L.lmhead_desc(M, H, V, dt, K)
-    add("lmhead_argmax", lambda: L.lmhead_argmax(d, dec.a, dec.lm_head, dec.seq_id, dec.round, dec.target.view(-1),
+    add("lmhead_argmax", lambda i: L.lmhead_argmax(d, dec.a, dec.lm_head, dec.seq_id, dec.round, dec.target.view(-1),
                                                  None, None, dec.lm_ws),
         2, (V * H + M * H) * esz, 2 * M * V * H)
-    add("rmsnorm", lambda: L.rmsnorm(M, H, dt, dec.x, Wl["attn_norm"], s.eps, dec.a), 4 * s.layers + 2,
+    add("rmsnorm", lambda i: L.rmsnorm(M, H, dt, dec.x, Ly[i]["attn_norm"], s.eps, dec.a), 4 * s.layers + 2,
         2 * M * H * esz, 0)
-    add("rope_kv_write", lambda: L.rope_kv_write(B, K, Hq, Hkv, D, dec.page, dec.max_pages, dt, dec.qkv, dec.rope,
+    add("rope_kv_write", lambda i: L.rope_kv_write(B, K, Hq, Hkv, D, dec.page, dec.max_pages, dt, dec.qkv, dec.rope,
                                                  dec.max_pos, dec.ctx_len, None, dec.q, dec.k_blk, dec.v_blk),
         2 * s.layers, (M * dec.nqkv + M * (Hq + 2 * Hkv) * D) * esz, 0)
     return tab
