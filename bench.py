@@ -57,48 +57,35 @@ def flush_caches():
     _FLUSH.sum()
 
 
-def event_time_ms(fn, iters=12):
-    """Median duration of one launch of `fn`, cold (caches flushed before each launch), timed with
-    HIP events on the current stream, the stream the library launches on."""
+def alternating_ms(fns, replays=5):
+    """Average duration of one launch over back-to-back launches of fns[0], fns[1], ... captured
+    in a HIP graph and replayed, timed with one pair of HIP events on the current stream."""
     import torch
-    fn()
-    times = []
-    for _ in range(iters):
-        flush_caches()
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
-        fn()
-        e.record()
-        torch.cuda.synchronize()
-        times.append(s.elapsed_time(e))
-    return float(np.median(times[2:]))
-
-
-def layer_sweep_ms(fn, n_layers, sweeps=4):
-    """Average duration of one launch of `fn(layer)` over back-to-back launches that walk every
-    layer's weights and caches in turn (as the round does).  One sweep over the layers is captured
-    in a HIP graph, so the launches follow each other on the GPU without host gaps, and the replays
-    are timed with one pair of HIP events on the current stream.  The layers' operands together
-    exceed the 256 MiB infinity cache, so each launch streams its own from HBM."""
-    import torch
-    for i in range(n_layers):
-        fn(i)
+    for f in fns:
+        f()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for i in range(n_layers):
-            fn(i)
+        for f in fns:
+            f()
     g.replay()
     torch.cuda.synchronize()
     flush_caches()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
-    for _ in range(sweeps):
+    for _ in range(replays):
         g.replay()
     e.record()
     torch.cuda.synchronize()
     del g
-    return s.elapsed_time(e) / (sweeps * n_layers)
+    return s.elapsed_time(e) / (replays * len(fns))
+
+
+def layer_sweep_ms(fn, n_layers, sweeps=4):
+    """Average duration of one launch of `fn(layer)` over back-to-back launches that walk every
+    layer's weights and caches in turn (as the round does).  The layers' operands together exceed
+    the 256 MiB infinity cache, so each launch streams its own from HBM."""
+    return alternating_ms([(lambda i=i: fn(i)) for i in range(n_layers)], sweeps)
 
 
 def kernel_table(dec, ctx_np):
@@ -191,7 +178,9 @@ def roofline_of(name, rec, bound="hbm"):
 
 def attention_roofline(kv_chunk):
     """Draft + verify attention at batch 16, 32Q/8KV heads, D 128, ragged contexts 512..16384,
-    16-token pages in a seeded random order (bf16 in, fp32 out); cold L2/MALL per launch."""
+    16-token pages in a seeded random order (bf16 in, fp32 out).  Launches alternate between two
+    copies of the paged cache (449 MB each, together 3.5x the 256 MiB infinity cache), so every
+    launch streams its keys and values from HBM; the per-launch time includes the chunk combine."""
     import torch
     import orthrus_round_amd as ora
     import synth
@@ -202,22 +191,27 @@ def attention_roofline(kv_chunk):
     maxp = inp.page_table.shape[1]
     desc = ora.attn_desc(16, 32, 8, 128, 32, 16, maxp, maxp * 16, kv_chunk, ora.BF16, ora.F32, 1.0)
     ws = torch.empty(max(16, ora.attn_workspace_bytes(desc)), dtype=torch.uint8, device="cuda")
-    q, pk, pv = dv(inp.q), dv(np.nan_to_num(inp.pages_k)), dv(np.nan_to_num(inp.pages_v))
+    q = dv(inp.q)
+    pages = [(dv(np.nan_to_num(inp.pages_k)), dv(np.nan_to_num(inp.pages_v)))]
+    pages.append((pages[0][0].clone(), pages[0][1].clone()))
     pt, cl = dv(inp.page_table, False), dv(inp.ctx, False)
     kb, vb = dv(inp.k_blk), dv(inp.v_blk)
     out = torch.empty((16, 32, 32, 128), dtype=torch.float32, device="cuda")
     res = {}
     n_sum = int(ctx.sum())
-    for name, fn, keys in [
-        ("draft", lambda: ora.draft_attn(desc, q, pk, pv, pt, cl, kb, vb, out, ws), n_sum + 16 * 32),
-        ("verify", lambda: ora.verify_attn(desc, q, pk, pv, pt, cl, out, ws), n_sum + 16 * 32),
+    for name, mk, keys in [
+        ("draft", lambda pk, pv: (lambda: ora.draft_attn(desc, q, pk, pv, pt, cl, kb, vb, out, ws)), n_sum + 16 * 32),
+        ("verify", lambda pk, pv: (lambda: ora.verify_attn(desc, q, pk, pv, pt, cl, out, ws)), n_sum + 16 * 32),
     ]:
         byts = keys * 8 * 128 * 2 * 2 + q.numel() * 2 + out.numel() * 4
-        ms = event_time_ms(fn, 20)
+        ms = alternating_ms([mk(pk, pv) for pk, pv in pages])
         res[name] = {"ms": round(ms, 5), "bytes": byts, "GBs": round(byts / ms / 1e6, 1),
                      "frac": round(byts / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    del pages
+    torch.cuda.empty_cache()
     return {"workload": "batch 16, 32Q/8KV, D128, ctx U[512,16384], 16-token paged random order, bf16->fp32, "
-                        "cold (512 MiB read before each launch)",
+                        "launches alternating between two copies of the cache (each streamed from HBM), "
+                        "attention + chunk combine per launch",
             "sum_ctx": n_sum, "kv_chunk": kv_chunk, **res}
 
 
