@@ -408,3 +408,34 @@ def test_gemm_is_repeatable_and_large_k_accurate():
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
     ref = a[:16].astype(np.float64) @ w.astype(np.float64).T
     assert np.abs(outs[0][:16] - ref).max() <= 1e-5 * np.abs(ref).max()
+
+
+def test_zero_sized_calls_launch_nothing():
+    """Empty batches and zero-row calls return OK and leave every output untouched."""
+    bf = torch.bfloat16
+    i32 = lambda v=7: torch.full((4,), v, dtype=torch.int32, device=DEV)
+    a = torch.zeros((1, 256), dtype=bf, device=DEV)
+    w = torch.zeros((512, 256), dtype=bf, device=DEV)
+    c = torch.full((1, 512), 3.0, dtype=bf, device=DEV)
+    ora.gemm(0, 512, 256, ora.BF16, ora.BF16, ora.EPI_STORE, a, w, None, c, gemm_ws(0, 512, 256, ora.BF16, ora.EPI_STORE))
+    y = torch.full((1, 256), 3.0, dtype=bf, device=DEV)
+    ora.rmsnorm(0, 256, ora.BF16, a, torch.ones(256, dtype=torch.float32, device=DEV), 1e-6, y)
+    d = ora.lmhead_desc(0, 256, 512, ora.BF16, 1)
+    tok = i32()
+    ora.lmhead_argmax(d, a, w, i32(0), i32(0), tok, None, None,
+                      torch.zeros(max(16, ora.lmhead_workspace_bytes(d)), dtype=torch.uint8, device=DEV))
+    desc = ora.attn_desc(0, 8, 2, 128, 32, 16, 4, 64)
+    ws = torch.zeros(max(16, ora.attn_workspace_bytes(desc)), dtype=torch.uint8, device=DEV)
+    q = torch.zeros((1, 32, 8, 128), dtype=bf, device=DEV)
+    pages = torch.zeros((4, 2, 16, 128), dtype=bf, device=DEV)
+    blk = torch.zeros((1, 32, 2, 128), dtype=bf, device=DEV)
+    out = torch.full((1, 32, 8, 128), 5.0, dtype=torch.float32, device=DEV)
+    pt = torch.zeros((1, 4), dtype=torch.int32, device=DEV)
+    ora.draft_attn(desc, q, pages, pages, pt, i32(0), blk, blk, out, ws)
+    ora.verify_attn(desc, q, pages, pages, pt, i32(0), out, ws)
+    st = [i32() for _ in range(7)]
+    outs = torch.full((1, 8), 7, dtype=torch.int32, device=DEV)
+    ora.consensus_commit(0, 32, st[0], st[1], st[2], st[3], st[4], outs, st[5], st[6], i32(), 8, 64)
+    torch.cuda.synchronize()
+    assert bool((c == 3.0).all()) and bool((y == 3.0).all()) and bool((tok == 7).all())
+    assert bool((out == 5.0).all()) and bool((outs == 7).all()) and all(bool((t == 7).all()) for t in st)
