@@ -188,12 +188,18 @@ typedef enum {
 } orthrus_epilogue_t;
 
 /* c [M, N'] = epilogue(a [M, K] . w [N, K]^T), fp32 accumulation.  K % 64 == 0; SwiGLU needs
- * N % 64 == 0.  The summation order of an output element depends on (N, K) only: for
- * N < 16384 the k-steps of a tile are dealt four ways inside one workgroup and the four
- * partial sums are added in a fixed order; for wider N each wave runs the k loop in order.
- * So a row computed alone has the same bits as the same row inside a larger batch.  The
- * workspace arguments are reserved: orthrus_gemm_workspace_bytes() returns 0 and NULL/0 may
- * be passed. */
+ * N % 64 == 0.  The summation order of an output element depends on (N, K) only, so a row
+ * computed alone has the same bits as the same row inside a larger batch:
+ *  - N < 16384 with K a multiple of 256 (bf16) or 128 (fp32): K is cut into four contiguous
+ *    quarters, each summed in k order into an fp32 partial, and the four partials are added in
+ *    quarter order before the epilogue;
+ *  - other N < 16384: the k-steps of a tile are dealt four ways inside one workgroup and the
+ *    four partial sums are added in a fixed order;
+ *  - N >= 16384: one k loop in order.
+ * Workspace: orthrus_gemm_workspace_bytes() bytes (4 * M * N * 4 for the quarter split, else 0),
+ * 16-byte aligned, caller-owned, contents undefined on entry and exit; a smaller workspace
+ * returns ORTHRUS_ERR_WORKSPACE before anything is launched.  Calls that overlap on one
+ * workspace race. */
 size_t orthrus_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t dtype,
                                     int32_t epilogue);
 int32_t orthrus_gemm(int32_t M, int32_t N, int32_t K, int32_t dtype, int32_t out_dtype,

@@ -1,9 +1,12 @@
 // Layer GEMMs of both views: C = epilogue(A W^T) on MFMA with fused residual add or SwiGLU.
 //
-// Decode-shaped GEMMs (M = batch x 32 rows, weights streamed from HBM once) use small output
-// tiles so that every shape has enough workgroups streaming weights; inside a workgroup the four
-// wavefronts split the k-steps four ways and sum their partial tiles in a fixed order, so results
-// are deterministic and a row's bits do not depend on the batch size.
+// Narrow outputs (N < 16384: the q/k/v, O and down projections) split K into four contiguous
+// quarters, one workgroup per (tile, quarter): each runs the plain MFMA chain over its quarter and
+// writes an fp32 partial tile, and a second kernel adds the four partials in quarter order and
+// applies the epilogue.  Splitting K across workgroups keeps 256+ workgroups busy with 128x128
+// tiles, which stream half the operand bytes of 64x64 tiles through L2.  Wide outputs (gate/up)
+// use plain tiles over the whole K.  Either way an output element's summation order depends on
+// (N, K) only, so results are deterministic and a row's bits do not depend on the batch size.
 #include "gemm_core.hpp"
 
 namespace orthrus {
@@ -71,8 +74,85 @@ __global__ __launch_bounds__(Cfg::NT) ORTHRUS_GEMM_WAVES void gemm_kernel(const 
   }
 }
 
-// Two families, chosen by N alone (so an output element's k order never depends on M):
-//  * N < 16384 (QKV, O, down projections): KsCfg tiles, k-steps split four ways per workgroup;
+// One k-quarter of a BM x BN tile: the plain MFMA chain over k in [q K/4, (q+1) K/4), stored as an
+// fp32 partial tile in P[q][M][N] straight from the accumulators (32 lanes write 32 consecutive
+// columns of one row).
+template <typename T, typename Cfg>
+__global__ __launch_bounds__(Cfg::NT) ORTHRUS_GEMM_WAVES void gemm_quarter_kernel(const T* __restrict__ A,
+                                                                                const T* __restrict__ W,
+                                                                                float* __restrict__ P, int M, int N,
+                                                                                int K) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int mtiles = (M + Cfg::BM - 1) / Cfg::BM;
+  int q, mt, nt;
+  xcd_tile_map(blockIdx.x, gridDim.x, 4, mtiles, q, mt, nt);
+  const int m0 = mt * Cfg::BM, n0 = nt * Cfg::BN, kq = K / 4;
+  f32x16 acc[Cfg::TM][Cfg::TN];
+  gemm_mainloop<T, Cfg>(A + (size_t)q * kq, W + (size_t)q * kq, M, N, K, m0, n0, smem, acc, kq);
+  const int lane = threadIdx.x & 63, hh = lane >> 5, r = lane & 31;
+  const int wu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wu / Cfg::WN, wn = wu % Cfg::WN;
+  float* Pq = P + (size_t)q * M * N;
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::TN; ++j) {
+      const int n = n0 + (wn * Cfg::TN + j) * 32 + r;
+      if (n >= N) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + (wm * Cfg::TM + i) * 32 + acc_row(e, hh);
+        if (m < M) Pq[(size_t)m * N + n] = acc[i][j][e];
+      }
+    }
+}
+
+// c = epilogue(P0 + P1 + P2 + P3), the partials added in quarter order.  V consecutive output
+// columns per thread (V = 4 when the row length allows 16-byte partial loads).  SwiGLU columns come
+// in (gate 32, up 32) groups, as in the plain epilogue.
+template <typename OutT, int EPI, int V>
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restrict__ P, const OutT* residual, OutT* C,
+                                                         int M, int N) {
+  const size_t MN = (size_t)M * N;
+  const int NO = EPI == ORTHRUS_EPI_SWIGLU ? N / 2 : N;
+  const size_t idx = ((size_t)blockIdx.x * 256 + threadIdx.x) * V;  // first of V outputs
+  if (idx >= (size_t)M * NO) return;
+  const int m = (int)(idx / NO), c = (int)(idx % NO);
+  auto sum = [&](int n, float (&s)[V]) {
+    const size_t o = (size_t)m * N + n;
+    if constexpr (V == 4) {
+      const f32x4 p0 = *reinterpret_cast<const f32x4*>(P + o), p1 = *reinterpret_cast<const f32x4*>(P + o + MN);
+      const f32x4 p2 = *reinterpret_cast<const f32x4*>(P + o + 2 * MN);
+      const f32x4 p3 = *reinterpret_cast<const f32x4*>(P + o + 3 * MN);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) s[v] = ((p0[v] + p1[v]) + p2[v]) + p3[v];
+    } else {
+      s[0] = ((P[o] + P[o + MN]) + P[o + 2 * MN]) + P[o + 3 * MN];
+    }
+  };
+  float x[V];
+  if constexpr (EPI == ORTHRUS_EPI_SWIGLU) {
+    const int ng = (c / 32) * 64 + c % 32;  // V divides 32: the V gate columns share a group
+    float g[V], u[V];
+    sum(ng, g);
+    sum(ng + 32, u);
+#pragma unroll
+    for (int v = 0; v < V; ++v) x[v] = g[v] / (1.0f + expf(-g[v])) * u[v];
+  } else {
+    sum(c, x);
+    if constexpr (EPI == ORTHRUS_EPI_RESIDUAL) {
+#pragma unroll
+      for (int v = 0; v < V; ++v) x[v] = to_f32(residual[idx + v]) + x[v];
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < V; ++v) C[idx + v] = from_f32<OutT>(x[v]);
+}
+
+// Families chosen by (N, K) alone (so an output element's k order never depends on M):
+//  * N < 16384 (QKV, O, down projections) with whole-stage quarters of K: plain tiles, one
+//    workgroup per (tile, k-quarter), partials added by gemm_reduce_kernel;
+//  * other N < 16384: KsCfg tiles, k-steps split four ways inside the workgroup;
 //  * N >= 16384 (the gate/up projection): plain GemmCfg tiles, waves split the output tile.
 // Within a family the tile height follows M only to avoid idle rows.
 // Ring depths (A stages, W stages) keep each configuration at or under 80 KiB of LDS, so two
@@ -128,9 +208,52 @@ int32_t launch_cfg(int M, int N, int K, int epi, const void* a, const void* w, c
   return check_launch("orthrus_gemm");
 }
 
+// The quarter split needs each quarter of K to be whole 128-byte stages.
+bool quarter_split(int N, int K, int dtype) {
+  const int bk = dtype == ORTHRUS_BF16 ? 64 : 32;
+  return N < kWideN && K % (4 * bk) == 0;
+}
+
+template <typename T, typename OutT, typename Cfg>
+int32_t launch_quarters(int M, int N, int K, int epi, const void* a, const void* w, const void* res, void* c,
+                        float* P, hipStream_t st) {
+  const int mtiles = (M + Cfg::BM - 1) / Cfg::BM, ntiles = (N + Cfg::BN - 1) / Cfg::BN;
+  const size_t lds = Cfg::RING;
+  allow_lds(gemm_quarter_kernel<T, Cfg>, lds);
+  hipLaunchKernelGGL((gemm_quarter_kernel<T, Cfg>), dim3(4 * mtiles * ntiles), dim3(Cfg::NT), lds, st,
+                     reinterpret_cast<const T*>(a), reinterpret_cast<const T*>(w), P, M, N, K);
+  const OutT* R = reinterpret_cast<const OutT*>(res);
+  OutT* C = reinterpret_cast<OutT*>(c);
+  const size_t outs = (size_t)M * (epi == ORTHRUS_EPI_SWIGLU ? N / 2 : N);
+  // 16-byte partial loads need every row to start on a 4-column boundary (SwiGLU: N % 64 == 0)
+  if (N % 4 == 0) {
+    const dim3 rgrid((unsigned)((outs / 4 + 255) / 256));
+    if (epi == ORTHRUS_EPI_STORE)
+      hipLaunchKernelGGL((gemm_reduce_kernel<OutT, ORTHRUS_EPI_STORE, 4>), rgrid, dim3(256), 0, st, P, R, C, M, N);
+    else if (epi == ORTHRUS_EPI_RESIDUAL)
+      hipLaunchKernelGGL((gemm_reduce_kernel<OutT, ORTHRUS_EPI_RESIDUAL, 4>), rgrid, dim3(256), 0, st, P, R, C, M, N);
+    else
+      hipLaunchKernelGGL((gemm_reduce_kernel<OutT, ORTHRUS_EPI_SWIGLU, 4>), rgrid, dim3(256), 0, st, P, R, C, M, N);
+  } else {
+    const dim3 rgrid((unsigned)((outs + 255) / 256));
+    if (epi == ORTHRUS_EPI_STORE)
+      hipLaunchKernelGGL((gemm_reduce_kernel<OutT, ORTHRUS_EPI_STORE, 1>), rgrid, dim3(256), 0, st, P, R, C, M, N);
+    else
+      hipLaunchKernelGGL((gemm_reduce_kernel<OutT, ORTHRUS_EPI_RESIDUAL, 1>), rgrid, dim3(256), 0, st, P, R, C, M, N);
+  }
+  return check_launch("orthrus_gemm");
+}
+
 template <typename T, typename OutT>
-int32_t launch(int M, int N, int K, int epi, const void* a, const void* w, const void* res, void* c, hipStream_t st) {
+int32_t launch(int M, int N, int K, int epi, const void* a, const void* w, const void* res, void* c, float* P,
+               hipStream_t st) {
+  constexpr int BK = 8 * (16 / (int)sizeof(T));  // k per 128-byte stage
   if (N < kWideN) {
+    if (K % (4 * BK) == 0) {
+      if (M <= 32) return launch_quarters<T, OutT, PlainSmall<T>>(M, N, K, epi, a, w, res, c, P, st);
+      if (M <= 64) return launch_quarters<T, OutT, PlainMid<T>>(M, N, K, epi, a, w, res, c, P, st);
+      return launch_quarters<T, OutT, PlainBig<T>>(M, N, K, epi, a, w, res, c, P, st);
+    }
     if (M <= 32) return launch_cfg<T, OutT, KsSmall<T>>(M, N, K, epi, a, w, res, c, st);
     return launch_cfg<T, OutT, KsBig<T>>(M, N, K, epi, a, w, res, c, st);
   }
@@ -167,24 +290,30 @@ int32_t validate(int32_t M, int32_t N, int32_t K, int32_t dtype, int32_t out_dty
 using namespace orthrus;
 
 extern "C" size_t orthrus_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t dtype, int32_t epilogue) {
-  (void)M; (void)N; (void)K; (void)dtype; (void)epilogue;
-  return 0;
+  (void)epilogue;
+  if (M <= 0 || N <= 0 || K <= 0 || !quarter_split(N, K, dtype)) return 0;
+  return (size_t)4 * M * N * sizeof(float);  // the four fp32 k-quarter partials
 }
 
 extern "C" int32_t orthrus_gemm(int32_t M, int32_t N, int32_t K, int32_t dtype, int32_t out_dtype, int32_t epilogue,
                                 const void* a, const void* w, const void* residual, void* c, void* workspace,
                                 size_t workspace_bytes, void* stream) {
-  (void)workspace; (void)workspace_bytes;
   if (int32_t s = validate(M, N, K, dtype, out_dtype, epilogue)) return s;
   ORTHRUS_REQUIRE(a && w && c, ORTHRUS_ERR_INVALID_ARG, "gemm: null pointer");
   ORTHRUS_REQUIRE(epilogue != ORTHRUS_EPI_RESIDUAL || residual, ORTHRUS_ERR_INVALID_ARG, "gemm: residual is null");
   if (M == 0) return ORTHRUS_OK;
+  const size_t need = orthrus_gemm_workspace_bytes(M, N, K, dtype, epilogue);
+  ORTHRUS_REQUIRE(need == 0 || (workspace && workspace_bytes >= need), ORTHRUS_ERR_WORKSPACE,
+                  "gemm: workspace %zu < %zu bytes", workspace ? workspace_bytes : (size_t)0, need);
+  ORTHRUS_REQUIRE(need == 0 || ((uintptr_t)workspace & 15) == 0, ORTHRUS_ERR_INVALID_ARG,
+                  "gemm: workspace not 16-byte aligned");
+  float* P = reinterpret_cast<float*>(workspace);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (dtype == ORTHRUS_BF16) {
-    if (out_dtype == ORTHRUS_BF16) return launch<bf16, bf16>(M, N, K, epilogue, a, w, residual, c, st);
-    return launch<bf16, float>(M, N, K, epilogue, a, w, residual, c, st);
+    if (out_dtype == ORTHRUS_BF16) return launch<bf16, bf16>(M, N, K, epilogue, a, w, residual, c, P, st);
+    return launch<bf16, float>(M, N, K, epilogue, a, w, residual, c, P, st);
   }
-  return launch<float, float>(M, N, K, epilogue, a, w, residual, c, st);
+  return launch<float, float>(M, N, K, epilogue, a, w, residual, c, P, st);
 }
 
 extern "C" int32_t orthrus_pack_gate_up(int32_t inter, int32_t hidden, int32_t dtype, const void* gate,

@@ -135,9 +135,11 @@ __device__ __forceinline__ void issue_stage(const T* src0, int row0, int lim, in
 
 // Shared main loop.  On return acc holds this wave's accumulators: its WM x WN share of the tile
 // (plain), or its k-quarter partial of the whole tile, already parked in LDS for ks4_sum (k-split).
+// K is the row stride of A and W; kext (default K) is how many k of each row the loop consumes,
+// starting at the given A and W pointers.
 template <typename T, typename Cfg, typename Acc>
 __device__ __forceinline__ void gemm_mainloop(const T* __restrict__ A, const T* __restrict__ W, int M, int N, int K,
-                                              int m0, int n0, unsigned char* lds, Acc& acc) {
+                                              int m0, int n0, unsigned char* lds, Acc& acc, int kext = -1) {
   using MF = Mfma<T>;
   constexpr int BK = Cfg::BK, EPC = Cfg::EPC, ROWB = Cfg::ROWB;
   constexpr int TM = Cfg::TM, TN = Cfg::TN, SA = Cfg::SA, SW = Cfg::SW;
@@ -232,7 +234,7 @@ __device__ __forceinline__ void gemm_mainloop(const T* __restrict__ A, const T* 
         for (int j = 0; j < TN; ++j) acc[i][j] = MF::mma(af[k * TM + i], bfr[k * TN + j], acc[i][j]);
   };
 
-  const int nk = K / BK;
+  const int nk = (kext < 0 ? K : kext) / BK;
   if (w_role) {
     for (int s = 0; s < SW - 1 && s < nk; ++s) issue_w(s);
   } else {

@@ -44,6 +44,7 @@ def test_struct_layouts_match_header():
     (lambda: ora.gemm(4, 64, 63, ora.BF16, ora.BF16, 0, 1, 1, None, 1, stream=0), 2),
     (lambda: ora.gemm(4, 64, 64, ora.BF16, ora.BF16, 1, 1, 1, None, 1, stream=0), 1),
     (lambda: ora.gemm(4, 64, 64, ora.F32, ora.BF16, 0, 1, 1, None, 1, stream=0), 2),
+    (lambda: ora.gemm(4, 64, 256, ora.BF16, ora.BF16, 0, 1, 1, None, 1, stream=0), 3),  # no workspace
     (lambda: ora.consensus_commit(2, 33, 1, 1, 1, 1, 1, 1, 1, 1, 1, 8, 64, stream=0), 1),
     (lambda: ora.rmsnorm(2, 64, 7, 1, 1, 1e-6, 1, stream=0), 1),
     (lambda: ora.rope_table(0, 64, 1e6, 1, stream=0), 1),
@@ -68,6 +69,12 @@ def test_attention_descriptor_validation():
             ora.verify_attn(d, 1, 1, 1, 1, 1, 1, None, stream=0)
 
 
-def test_gemm_needs_no_workspace():
-    assert ora.gemm_workspace_bytes(256, 4096, 4096, ora.BF16, ora.EPI_STORE) == 0
+def test_gemm_workspace_holds_the_k_quarter_partials():
+    # N < 16384 with whole-stage quarters of K: four fp32 partial tiles of [M, N]
+    assert ora.gemm_workspace_bytes(256, 4096, 4096, ora.BF16, ora.EPI_STORE) == 4 * 256 * 4096 * 4
+    assert ora.gemm_workspace_bytes(8, 6144, 4096, ora.F32, ora.EPI_RESIDUAL) == 4 * 8 * 6144 * 4
+    assert ora.gemm_workspace_bytes(8, 6144, 128, ora.F32, ora.EPI_STORE) == 4 * 8 * 6144 * 4
+    # the wide (gate/up) family and K that does not split into whole 128-byte stages need none
     assert ora.gemm_workspace_bytes(8, 24576, 4096, ora.BF16, ora.EPI_SWIGLU) == 0
+    assert ora.gemm_workspace_bytes(8, 4096, 192, ora.BF16, ora.EPI_STORE) == 0
+    assert ora.gemm_workspace_bytes(0, 4096, 4096, ora.BF16, ora.EPI_STORE) == 0
