@@ -109,12 +109,14 @@ def kernel_table(dec, ctx_np):
 
     add("gemm_qkv", lambda i: L.gemm(M, dec.nqkv, H, dt, dt, L.EPI_STORE, dec.a, Ly[i]["qkv_ar"], None, dec.qkv, dec.gemm_ws),
         2 * s.layers, (dec.nqkv * H + M * H + M * dec.nqkv) * esz, 2 * M * dec.nqkv * H)
-    add("gemm_o_residual", lambda i: L.gemm(M, H, Hq * D, dt, dt, L.EPI_RESIDUAL, dec.o, Ly[i]["o_ar"], dec.x, dec.x, dec.gemm_ws),
-        2 * s.layers, (H * Hq * D + M * Hq * D + 2 * M * H) * esz, 2 * M * H * Hq * D)
+    add("gemm_o_residual_rmsnorm", lambda i: L.gemm_residual_rmsnorm(M, H, Hq * D, dt, dec.o, Ly[i]["o_ar"], dec.x,
+                                                                     Ly[i]["mlp_norm"], s.eps, dec.a, dec.gemm_ws),
+        2 * s.layers, (H * Hq * D + M * Hq * D + 3 * M * H) * esz, 2 * M * H * Hq * D)
     add("gemm_gate_up_swiglu", lambda i: L.gemm(M, 2 * I, H, dt, dt, L.EPI_SWIGLU, dec.a, Ly[i]["gate_up"], None, dec.h, dec.gemm_ws),
         2 * s.layers, (2 * I * H + M * H + M * I) * esz, 2 * M * 2 * I * H)
-    add("gemm_down_residual", lambda i: L.gemm(M, H, I, dt, dt, L.EPI_RESIDUAL, dec.h, Ly[i]["down"], dec.x, dec.x, dec.gemm_ws),
-        2 * s.layers, (H * I + M * I + 2 * M * H) * esz, 2 * M * H * I)
+    add("gemm_down_residual_rmsnorm", lambda i: L.gemm_residual_rmsnorm(M, H, I, dt, dec.h, Ly[i]["down"], dec.x,
+                                                                        Ly[i]["attn_norm"], s.eps, dec.a, dec.gemm_ws),
+        2 * s.layers, (H * I + M * I + 3 * M * H) * esz, 2 * M * H * I)
     kv_b = Hkv * D * 2 * esz  # K and V bytes per key
     qo_b = 2 * M * Hq * D * esz
     add("attn_draft", lambda i: L.draft_attn(desc, dec.q, dec.k_pages[i], dec.v_pages[i], dec.page_table, dec.ctx_len,
@@ -127,7 +129,7 @@ def kernel_table(dec, ctx_np):
     add("lmhead_argmax", lambda i: L.lmhead_argmax(d, dec.a, dec.lm_head, dec.seq_id, dec.round, dec.target.view(-1),
                                                  None, None, dec.lm_ws),
         2, (V * H + M * H) * esz, 2 * M * V * H)
-    add("rmsnorm", lambda i: L.rmsnorm(M, H, dt, dec.x, Ly[i]["attn_norm"], s.eps, dec.a), 4 * s.layers + 2,
+    add("rmsnorm", lambda i: L.rmsnorm(M, H, dt, dec.x, Ly[i]["attn_norm"], s.eps, dec.a), 2,
         2 * M * H * esz, 0)
     add("rope_kv_write", lambda i: L.rope_kv_write(B, K, Hq, Hkv, D, dec.page, dec.max_pages, dt, dec.qkv, dec.rope,
                                                  dec.max_pos, dec.ctx_len, None, dec.q, dec.k_blk, dec.v_blk),

@@ -206,6 +206,18 @@ int32_t orthrus_gemm(int32_t M, int32_t N, int32_t K, int32_t dtype, int32_t out
                      int32_t epilogue, const void* a, const void* w, const void* residual, void* c,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* The residual GEMM and the RMSNorm that follows it in the layer body, in one call:
+ *   x [M, N] = x + a [M, K] . w [N, K]^T   (in place, the residual stream, `dtype`)
+ *   y [M, N] = x / sqrt(mean(x^2) + eps) * gain   (gain fp32 [N]; y in `dtype`)
+ * The result has exactly the bits of orthrus_gemm(..., ORTHRUS_EPI_RESIDUAL, residual = c = x) followed
+ * by orthrus_rmsnorm(M, N, dtype, x, gain, eps, y).  Where the GEMM takes the k-quarter split and a
+ * row is at most 1024 16-byte chunks (x, y 16-byte aligned), the quarter partials are added, the
+ * residual updated and the row normalised in one pass; otherwise the two calls run in sequence.
+ * Workspace as orthrus_gemm with ORTHRUS_EPI_RESIDUAL; y must not overlap x. */
+int32_t orthrus_gemm_residual_rmsnorm(int32_t M, int32_t N, int32_t K, int32_t dtype, const void* a,
+                                      const void* w, void* x, const float* gain, float eps, void* y,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* Interleave gate [I, H] and up [I, H] into [2I, H] in 32-row groups: gate 0..31, up 0..31,
  * gate 32..63, ... (I % 32 == 0). */
 int32_t orthrus_pack_gate_up(int32_t inter, int32_t hidden, int32_t dtype, const void* gate,

@@ -58,6 +58,7 @@ _SIGS = {
                                   _P, _P, _I32, _I32, _P, _SZ, _P], _I32),
     "orthrus_gemm_workspace_bytes": ([_I32, _I32, _I32, _I32, _I32], _SZ),
     "orthrus_gemm": ([_I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P], _I32),
+    "orthrus_gemm_residual_rmsnorm": ([_I32, _I32, _I32, _I32, _P, _P, _P, _P, _F32, _P, _P, _SZ, _P], _I32),
     "orthrus_pack_gate_up": ([_I32, _I32, _I32, _P, _P, _P, _P], _I32),
     "orthrus_rmsnorm": ([_I32, _I32, _I32, _P, _P, _F32, _P, _P], _I32),
     "orthrus_rope_table": ([_I32, _I32, ctypes.c_double, _P, _P], _I32),
@@ -169,6 +170,12 @@ def gemm(M, N, K, dtype, out_dtype, epilogue, a, w, residual, c, ws=None, stream
     _check(lib().orthrus_gemm(M, N, K, dtype, out_dtype, epilogue, _ptr(a), _ptr(w), _ptr(residual), _ptr(c),
                               _ptr(ws), 0 if ws is None or isinstance(ws, int) else ws.numel() * ws.element_size(),
                               _stream(stream)))
+
+
+def gemm_residual_rmsnorm(M, N, K, dtype, a, w, x, gain, eps, y, ws=None, stream=None):
+    _check(lib().orthrus_gemm_residual_rmsnorm(M, N, K, dtype, _ptr(a), _ptr(w), _ptr(x), _ptr(gain), eps, _ptr(y),
+                                               _ptr(ws), 0 if ws is None or isinstance(ws, int)
+                                               else ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def pack_gate_up(inter, hidden, dtype, gate, up, packed, stream=None):

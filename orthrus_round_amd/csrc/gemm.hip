@@ -149,6 +149,77 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restric
   for (int v = 0; v < V; ++v) C[idx + v] = from_f32<OutT>(x[v]);
 }
 
+// The residual k-quarter reduce fused with the RMSNorm that follows every residual GEMM of a layer:
+// x = x + (P0 + P1 + P2 + P3) (stored), then y = rmsnorm(x) * g.  One workgroup per row.  Each thread
+// owns the same 16-byte chunks of the row as rmsnorm_kernel (chunk c = q * 256 + tid) and the sum of
+// squares runs over the stored (rounded) x in the same order (per thread in chunk order, a wave
+// butterfly, then the four waves in order), so the result has the bits of the residual GEMM
+// followed by orthrus_rmsnorm.
+template <typename T>
+__global__ __launch_bounds__(256) void gemm_reduce_rmsnorm_kernel(const float* __restrict__ P, T* x,
+                                                                  const float* __restrict__ g, float eps, int M,
+                                                                  int N, T* __restrict__ y) {
+  constexpr int EPC = 16 / sizeof(T), NCH = 4;
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  __shared__ float red[4];
+  const int m = blockIdx.x, tid = threadIdx.x;
+  const size_t MN = (size_t)M * N;
+  T* xr = x + (size_t)m * N;
+  T* yr = y + (size_t)m * N;
+  const float* pr = P + (size_t)m * N;
+  const int nch = N / EPC;
+  u32x4_t buf[NCH];
+#pragma unroll
+  for (int q = 0; q < NCH; ++q) {
+    const int c = q * 256 + tid;
+    if (c < nch) {
+      const u32x4_t rv = *reinterpret_cast<const u32x4_t*>(xr + (size_t)c * EPC);
+      const T* re = reinterpret_cast<const T*>(&rv);
+      T* xe = reinterpret_cast<T*>(&buf[q]);
+#pragma unroll
+      for (int i = 0; i < EPC; i += 4) {
+        const size_t o = (size_t)c * EPC + i;
+        const f32x4 p0 = *reinterpret_cast<const f32x4*>(pr + o), p1 = *reinterpret_cast<const f32x4*>(pr + o + MN);
+        const f32x4 p2 = *reinterpret_cast<const f32x4*>(pr + o + 2 * MN);
+        const f32x4 p3 = *reinterpret_cast<const f32x4*>(pr + o + 3 * MN);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) xe[i + v] = from_f32<T>(to_f32(re[i + v]) + (((p0[v] + p1[v]) + p2[v]) + p3[v]));
+      }
+      *reinterpret_cast<u32x4_t*>(xr + (size_t)c * EPC) = buf[q];
+    }
+  }
+  float ss = 0.0f;
+#pragma unroll
+  for (int q = 0; q < NCH; ++q) {
+    const int c = q * 256 + tid;
+    if (c < nch) {
+      const T* e = reinterpret_cast<const T*>(&buf[q]);
+#pragma unroll
+      for (int i = 0; i < EPC; ++i) {
+        const float v = to_f32(e[i]);
+        ss += v * v;
+      }
+    }
+  }
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  const float inv = 1.0f / sqrtf(tot / (float)N + eps);
+#pragma unroll
+  for (int q = 0; q < NCH; ++q) {
+    const int c = q * 256 + tid;
+    if (c < nch) {
+      const T* e = reinterpret_cast<const T*>(&buf[q]);
+      u32x4_t o;
+      T* oe = reinterpret_cast<T*>(&o);
+#pragma unroll
+      for (int i = 0; i < EPC; ++i) oe[i] = from_f32<T>(to_f32(e[i]) * inv * g[(size_t)c * EPC + i]);
+      *reinterpret_cast<u32x4_t*>(yr + (size_t)c * EPC) = o;
+    }
+  }
+}
+
 // Families chosen by (N, K) alone (so an output element's k order never depends on M):
 //  * N < 16384 (QKV, O, down projections) with whole-stage quarters of K: plain tiles, one
 //    workgroup per (tile, k-quarter), partials added by gemm_reduce_kernel;
@@ -263,6 +334,42 @@ int32_t launch(int M, int N, int K, int epi, const void* a, const void* w, const
   return launch_cfg<T, OutT, ORTHRUS_WIDE_HUGE_CFG(T)>(M, N, K, epi, a, w, res, c, st);
 }
 
+// The fused residual + RMSNorm pass applies when the GEMM takes the quarter split and the row fits
+// rmsnorm_kernel's register path (16-byte chunks, at most 1024 of them, 16-byte aligned rows).
+template <typename T>
+bool fused_norm_ok(int N, int K, int dtype, const void* x, const void* y) {
+  constexpr int EPC = 16 / (int)sizeof(T);
+  return quarter_split(N, K, dtype) && N % EPC == 0 && N / EPC <= 4 * 256 &&
+         ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15) == 0;
+}
+
+template <typename T>
+int32_t launch_residual_rmsnorm(int M, int N, int K, const void* a, const void* w, void* x, const float* gain,
+                                float eps, void* y, float* P, hipStream_t st) {
+  using Cfg = PlainBig<T>;
+  if (M <= 32) {
+    using C = PlainSmall<T>;
+    const int nt = (N + C::BN - 1) / C::BN, mt = (M + C::BM - 1) / C::BM;
+    allow_lds(gemm_quarter_kernel<T, C>, C::RING);
+    hipLaunchKernelGGL((gemm_quarter_kernel<T, C>), dim3(4 * mt * nt), dim3(C::NT), C::RING, st,
+                       reinterpret_cast<const T*>(a), reinterpret_cast<const T*>(w), P, M, N, K);
+  } else if (M <= 64) {
+    using C = PlainMid<T>;
+    const int nt = (N + C::BN - 1) / C::BN, mt = (M + C::BM - 1) / C::BM;
+    allow_lds(gemm_quarter_kernel<T, C>, C::RING);
+    hipLaunchKernelGGL((gemm_quarter_kernel<T, C>), dim3(4 * mt * nt), dim3(C::NT), C::RING, st,
+                       reinterpret_cast<const T*>(a), reinterpret_cast<const T*>(w), P, M, N, K);
+  } else {
+    const int nt = (N + Cfg::BN - 1) / Cfg::BN, mt = (M + Cfg::BM - 1) / Cfg::BM;
+    allow_lds(gemm_quarter_kernel<T, Cfg>, Cfg::RING);
+    hipLaunchKernelGGL((gemm_quarter_kernel<T, Cfg>), dim3(4 * mt * nt), dim3(Cfg::NT), Cfg::RING, st,
+                       reinterpret_cast<const T*>(a), reinterpret_cast<const T*>(w), P, M, N, K);
+  }
+  hipLaunchKernelGGL(gemm_reduce_rmsnorm_kernel<T>, dim3(M), dim3(256), 0, st, P, reinterpret_cast<T*>(x), gain, eps,
+                     M, N, reinterpret_cast<T*>(y));
+  return check_launch("orthrus_gemm_residual_rmsnorm");
+}
+
 template <typename T>
 __global__ void pack_gate_up_kernel(const T* g, const T* u, T* p, int inter, int hidden) {
   const int row = blockIdx.x;  // 0 .. 2*inter-1 of the packed matrix
@@ -314,6 +421,30 @@ extern "C" int32_t orthrus_gemm(int32_t M, int32_t N, int32_t K, int32_t dtype, 
     return launch<bf16, float>(M, N, K, epilogue, a, w, residual, c, P, st);
   }
   return launch<float, float>(M, N, K, epilogue, a, w, residual, c, P, st);
+}
+
+extern "C" int32_t orthrus_gemm_residual_rmsnorm(int32_t M, int32_t N, int32_t K, int32_t dtype, const void* a,
+                                                 const void* w, void* x, const float* gain, float eps, void* y,
+                                                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (int32_t s = validate(M, N, K, dtype, dtype, ORTHRUS_EPI_RESIDUAL)) return s;
+  ORTHRUS_REQUIRE(a && w && x && gain && y, ORTHRUS_ERR_INVALID_ARG, "gemm_residual_rmsnorm: null pointer");
+  if (M == 0) return ORTHRUS_OK;
+  const size_t need = orthrus_gemm_workspace_bytes(M, N, K, dtype, ORTHRUS_EPI_RESIDUAL);
+  ORTHRUS_REQUIRE(need == 0 || (workspace && workspace_bytes >= need), ORTHRUS_ERR_WORKSPACE,
+                  "gemm_residual_rmsnorm: workspace %zu < %zu bytes", workspace ? workspace_bytes : (size_t)0, need);
+  ORTHRUS_REQUIRE(need == 0 || ((uintptr_t)workspace & 15) == 0, ORTHRUS_ERR_INVALID_ARG,
+                  "gemm_residual_rmsnorm: workspace not 16-byte aligned");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  float* P = reinterpret_cast<float*>(workspace);
+  if (dtype == ORTHRUS_BF16 && fused_norm_ok<bf16>(N, K, dtype, x, y))
+    return launch_residual_rmsnorm<bf16>(M, N, K, a, w, x, gain, eps, y, P, st);
+  if (dtype == ORTHRUS_F32 && fused_norm_ok<float>(N, K, dtype, x, y))
+    return launch_residual_rmsnorm<float>(M, N, K, a, w, x, gain, eps, y, P, st);
+  // other shapes: the two calls in sequence (the fused pass has their bits)
+  if (int32_t s = orthrus_gemm(M, N, K, dtype, dtype, ORTHRUS_EPI_RESIDUAL, a, w, x, x, workspace, workspace_bytes,
+                               stream))
+    return s;
+  return orthrus_rmsnorm(M, N, dtype, x, gain, eps, y, stream);
 }
 
 extern "C" int32_t orthrus_pack_gate_up(int32_t inter, int32_t hidden, int32_t dtype, const void* gate,

@@ -159,8 +159,11 @@ class Decoder:
         desc = self._attn_desc(nb, kb)
         ws = self._ws(desc)
         x, a = self.x[:M], self.a[:M]
+        # every residual GEMM also normalises its rows for the next block (the next layer's
+        # attention norm, or the final norm before the LM head), so `a` is ready at each step
+        L.rmsnorm(M, H, dt, x, self.layers[0]["attn_norm"], s.eps, a)
         for l, Wl in enumerate(self.layers):
-            L.rmsnorm(M, H, dt, x, Wl["attn_norm"], s.eps, a)
+            nxt = self.layers[l + 1]["attn_norm"] if l + 1 < len(self.layers) else self.final_norm
             L.gemm(M, self.nqkv, H, dt, dt, L.EPI_STORE, a, Wl["qkv_" + view], None, self.qkv, self.gemm_ws)
             if draft:
                 L.rope_kv_write(nb, kb, Hq, Hkv, D, self.page, self.max_pages, dt, self.qkv, self.rope,
@@ -171,15 +174,15 @@ class Decoder:
                 L.rope_kv_write(nb, kb, Hq, Hkv, D, self.page, self.max_pages, dt, self.qkv, self.rope,
                                 self.max_pos, ctx, self.page_table, self.q, self.k_pages[l], self.v_pages[l])
                 L.verify_attn(desc, self.q, self.k_pages[l], self.v_pages[l], self.page_table, ctx, self.o, ws)
-            L.gemm(M, H, Hq * D, dt, dt, L.EPI_RESIDUAL, self.o, Wl["o_" + view], x, x, self.gemm_ws)
-            L.rmsnorm(M, H, dt, x, Wl["mlp_norm"], s.eps, a)
+            L.gemm_residual_rmsnorm(M, H, Hq * D, dt, self.o, Wl["o_" + view], x, Wl["mlp_norm"], s.eps, a,
+                                    self.gemm_ws)
             L.gemm(M, 2 * I, H, dt, dt, L.EPI_SWIGLU, a, Wl["gate_up"], None, self.h, self.gemm_ws)
-            L.gemm(M, H, I, dt, dt, L.EPI_RESIDUAL, self.h, Wl["down"], x, x, self.gemm_ws)
+            L.gemm_residual_rmsnorm(M, H, I, dt, self.h, Wl["down"], x, nxt, s.eps, a, self.gemm_ws)
 
     def _lm_head(self, nb, kb, tokens, temperature=0.0, seed=0, stream_id=L.STREAM_DRAFT, logits=None, lse=None):
         s = self.shape
         M = nb * kb
-        L.rmsnorm(M, s.hidden, self.dt, self.x[:M], self.final_norm, s.eps, self.a[:M])
+        # self.a[:M] already holds final_norm(x): the last layer's down projection wrote it
         d = L.lmhead_desc(M, s.hidden, s.vocab, self.dt, kb, stream_id, temperature, seed)
         L.lmhead_argmax(d, self.a[:M], self.lm_head, self.seq_id, self.round, tokens, logits, lse, self.lm_ws)
 

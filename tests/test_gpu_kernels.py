@@ -440,3 +440,28 @@ def test_zero_sized_calls_launch_nothing():
     torch.cuda.synchronize()
     assert bool((c == 3.0).all()) and bool((y == 3.0).all()) and bool((tok == 7).all())
     assert bool((out == 5.0).all()) and bool((outs == 7).all()) and all(bool((t == 7).all()) for t in st)
+
+
+@pytest.mark.parametrize("dtype", [ora.BF16, ora.F32])
+@pytest.mark.parametrize("M,N,K", [(256, 4096, 4096), (8, 4096, 12288), (45, 1024, 256), (17, 320, 128)])
+def test_gemm_residual_rmsnorm_has_the_bits_of_the_two_calls(dtype, M, N, K):
+    """The fused residual GEMM + RMSNorm (one pass over the rows where the shapes allow, the two calls
+    in sequence otherwise) gives exactly the bits of orthrus_gemm(RESIDUAL) then orthrus_rmsnorm."""
+    bf = dtype == ora.BF16
+    a, w = synth.lmhead_inputs(27, M, K, N, h_std=1.0, w_std=0.02, bf16=bf)
+    x0 = synth.lmhead_inputs(28, M, N, 8, bf16=bf)[0]
+    gain = dev(np.random.default_rng(29).uniform(0.5, 1.5, N).astype(np.float32))
+    ws = gemm_ws(M, N, K, dtype, ora.EPI_RESIDUAL)
+    tdt = torch.bfloat16 if bf else torch.float32
+    xs, ys = dev(x0, dtype), torch.empty((M, N), dtype=tdt, device=DEV)
+    ora.gemm(M, N, K, dtype, dtype, ora.EPI_RESIDUAL, dev(a, dtype), dev(w, dtype), xs, xs, ws)
+    ora.rmsnorm(M, N, dtype, xs, gain, 1e-6, ys)
+    xf, yf = dev(x0, dtype), torch.empty((M, N), dtype=tdt, device=DEV)
+    ora.gemm_residual_rmsnorm(M, N, K, dtype, dev(a, dtype), dev(w, dtype), xf, gain, 1e-6, yf, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(xs, xf) and torch.equal(ys, yf)
+    # and the result is the residual update and the norm
+    z = x0.astype(np.float64) + a.astype(np.float64) @ w.astype(np.float64).T
+    ref = z / np.sqrt((z ** 2).mean(1, keepdims=True) + 1e-6) * gain.cpu().numpy()
+    out = yf.float().cpu().numpy()
+    assert np.abs(out - ref).max() / np.abs(ref).max() <= (2e-2 if bf else 1e-5)
