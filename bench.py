@@ -107,7 +107,9 @@ def kernel_table(dec, ctx_np):
         ms = layer_sweep_ms(fn, nl)
         tab[name] = dict(ms=ms, per_round=per_round, bytes=bytes_, flops=flops)
 
-    add("gemm_qkv", lambda i: L.gemm(M, dec.nqkv, H, dt, dt, L.EPI_STORE, dec.a, Ly[i]["qkv_ar"], None, dec.qkv, dec.gemm_ws),
+    add("gemm_qkv_rope_kv", lambda i: L.gemm_rope_kv_write(B, K, Hq, Hkv, D, dec.page, dec.max_pages, H, dt, dec.a,
+                                                          Ly[i]["qkv_ar"], dec.rope, dec.max_pos, dec.ctx_len, None,
+                                                          dec.qkv, dec.q, dec.k_blk, dec.v_blk, dec.gemm_ws),
         2 * s.layers, (dec.nqkv * H + M * H + M * dec.nqkv) * esz, 2 * M * dec.nqkv * H)
     add("gemm_o_residual_rmsnorm", lambda i: L.gemm_residual_rmsnorm(M, H, Hq * D, dt, dec.o, Ly[i]["o_ar"], dec.x,
                                                                      Ly[i]["mlp_norm"], s.eps, dec.a, dec.gemm_ws),
@@ -131,9 +133,6 @@ def kernel_table(dec, ctx_np):
         2, (V * H + M * H) * esz, 2 * M * V * H)
     add("rmsnorm", lambda i: L.rmsnorm(M, H, dt, dec.x, Ly[i]["attn_norm"], s.eps, dec.a), 2,
         2 * M * H * esz, 0)
-    add("rope_kv_write", lambda i: L.rope_kv_write(B, K, Hq, Hkv, D, dec.page, dec.max_pages, dt, dec.qkv, dec.rope,
-                                                 dec.max_pos, dec.ctx_len, None, dec.q, dec.k_blk, dec.v_blk),
-        2 * s.layers, (M * dec.nqkv + M * (Hq + 2 * Hkv) * D) * esz, 0)
     return tab
 
 

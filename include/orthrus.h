@@ -231,6 +231,21 @@ int32_t orthrus_rmsnorm(int32_t rows, int32_t hidden, int32_t dtype, const void*
 int32_t orthrus_rope_table(int32_t max_pos, int32_t head_dim, double base, float* table,
                            void* stream);
 
+/* The QKV projection and the RoPE + K/V write that follows it in the layer body, in one call:
+ * qkv = a [batch*block, hidden] . w [(Hq + 2 Hkv) * D, hidden]^T, then orthrus_rope_kv_write on it.
+ * The result has exactly the bits of orthrus_gemm(..., ORTHRUS_EPI_STORE, c = qkv) followed by
+ * orthrus_rope_kv_write(..., qkv, ...).  Where the GEMM takes the k-quarter split, the partials are
+ * added, rotated and written row by row and `qkv` is not touched; otherwise the two calls run in
+ * sequence through `qkv` (caller-owned [batch*block, (Hq + 2 Hkv) * D], contents undefined after).
+ * Workspace as orthrus_gemm with ORTHRUS_EPI_STORE. */
+int32_t orthrus_gemm_rope_kv_write(int32_t batch, int32_t block, int32_t q_heads, int32_t kv_heads,
+                                   int32_t head_dim, int32_t page_size, int32_t max_pages,
+                                   int32_t hidden, int32_t dtype, const void* a, const void* w,
+                                   const float* rope_table, int32_t max_pos, const int32_t* ctx_len,
+                                   const int32_t* page_table, void* qkv, void* q_out, void* k_dst,
+                                   void* v_dst, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
 /* Split a QKV projection [batch*block, (Hq + 2 Hkv) * D] (q | k | v), apply rotate-half RoPE at
  * positions ctx_len[b] + s to q and k, write q_out [batch*block, Hq*D] and K/V either into the
  * paged cache at positions [ctx_len[b], ctx_len[b] + block) (page_table != NULL) or into

@@ -58,6 +58,8 @@ _SIGS = {
                                   _P, _P, _I32, _I32, _P, _SZ, _P], _I32),
     "orthrus_gemm_workspace_bytes": ([_I32, _I32, _I32, _I32, _I32], _SZ),
     "orthrus_gemm": ([_I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P], _I32),
+    "orthrus_gemm_rope_kv_write": ([_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I32, _P,
+                                    _P, _P, _P, _P, _P, _P, _SZ, _P], _I32),
     "orthrus_gemm_residual_rmsnorm": ([_I32, _I32, _I32, _I32, _P, _P, _P, _P, _F32, _P, _P, _SZ, _P], _I32),
     "orthrus_pack_gate_up": ([_I32, _I32, _I32, _P, _P, _P, _P], _I32),
     "orthrus_rmsnorm": ([_I32, _I32, _I32, _P, _P, _F32, _P, _P], _I32),
@@ -176,6 +178,15 @@ def gemm_residual_rmsnorm(M, N, K, dtype, a, w, x, gain, eps, y, ws=None, stream
     _check(lib().orthrus_gemm_residual_rmsnorm(M, N, K, dtype, _ptr(a), _ptr(w), _ptr(x), _ptr(gain), eps, _ptr(y),
                                                _ptr(ws), 0 if ws is None or isinstance(ws, int)
                                                else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def gemm_rope_kv_write(batch, block, q_heads, kv_heads, head_dim, page_size, max_pages, hidden, dtype, a, w, table,
+                       max_pos, ctx_len, page_table, qkv, q_out, k_dst, v_dst, ws=None, stream=None):
+    _check(lib().orthrus_gemm_rope_kv_write(batch, block, q_heads, kv_heads, head_dim, page_size, max_pages, hidden,
+                                            dtype, _ptr(a), _ptr(w), _ptr(table), max_pos, _ptr(ctx_len),
+                                            _ptr(page_table), _ptr(qkv), _ptr(q_out), _ptr(k_dst), _ptr(v_dst),
+                                            _ptr(ws), 0 if ws is None or isinstance(ws, int)
+                                            else ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def pack_gate_up(inter, hidden, dtype, gate, up, packed, stream=None):

@@ -220,6 +220,68 @@ __global__ __launch_bounds__(256) void gemm_reduce_rmsnorm_kernel(const float* _
   }
 }
 
+// The q/k/v k-quarter reduce fused with RoPE and the K/V write (rope_kv_kernel's work): every q/k/v
+// element is the sum of the four partials in quarter order rounded to T, exactly the value the store
+// epilogue would have written, and the rotation and the writes are rope_kv_kernel's, so the result has
+// the bits of orthrus_gemm(STORE) followed by orthrus_rope_kv_write.  Workgroup (row m, head group y)
+// handles 256 / (D/2) consecutive heads of the row's Hq + Hkv rotated heads and Hkv value heads, one
+// rotation pair (or two copied value elements) per thread.
+template <typename T>
+__global__ __launch_bounds__(256) void gemm_reduce_rope_kv_kernel(const float* __restrict__ P, int M,
+                                                                  const float* __restrict__ table, int max_pos,
+                                                                  const int32_t* __restrict__ ctx_len,
+                                                                  const int32_t* __restrict__ page_table, int block,
+                                                                  int Hq, int Hkv, int D, int page, int max_pages,
+                                                                  T* __restrict__ q_out, T* __restrict__ k_dst,
+                                                                  T* __restrict__ v_dst) {
+  const int m = blockIdx.x, b = m / block, s = m % block;
+  const int half = D / 2, hpw = 256 / half;  // heads per workgroup
+  const int hd = blockIdx.y * hpw + (int)threadIdx.x / half, i = (int)threadIdx.x % half;
+  if (hd >= Hq + 2 * Hkv) return;
+  const int pos = ctx_len[b] + s;
+  const int width = (Hq + 2 * Hkv) * D;
+  const size_t MN = (size_t)M * width;
+  const float* pr = P + (size_t)m * width;
+  auto val = [&](int j) {
+    return to_f32(from_f32<T>(((pr[j] + pr[j + MN]) + pr[j + 2 * MN]) + pr[j + 3 * MN]));
+  };
+  const bool pos_ok = pos >= 0 && pos < max_pos;
+  size_t kv_base = 0;
+  bool kv_ok = pos_ok;
+  if (page_table) {
+    kv_ok = kv_ok && pos < max_pages * page;
+    if (kv_ok) {
+      const int pg = page_table[(size_t)b * max_pages + pos / page];
+      kv_base = ((size_t)pg * Hkv * page + (pos % page)) * D;
+    }
+  } else {
+    kv_base = (size_t)m * Hkv * D;
+  }
+  const size_t kv_head_stride = page_table ? (size_t)page * D : (size_t)D;
+  if (hd < Hq + Hkv) {
+    const float* cs = table + (size_t)(pos_ok ? pos : 0) * half * 2;
+    const float c = cs[2 * i], sn = cs[2 * i + 1];
+    const float x1 = val(hd * D + i), x2 = val(hd * D + i + half);
+    const float y1 = pos_ok ? x1 * c - x2 * sn : __builtin_nanf("");
+    const float y2 = pos_ok ? x2 * c + x1 * sn : __builtin_nanf("");
+    if (hd < Hq) {
+      T* qo = q_out + (size_t)m * Hq * D + hd * D;
+      qo[i] = from_f32<T>(y1);
+      qo[i + half] = from_f32<T>(y2);
+    } else if (kv_ok) {
+      T* ko = k_dst + kv_base + (hd - Hq) * kv_head_stride;
+      ko[i] = from_f32<T>(y1);
+      ko[i + half] = from_f32<T>(y2);
+    }
+  } else if (kv_ok) {
+    const int hk = hd - Hq - Hkv;
+    T* vo = v_dst + kv_base + hk * kv_head_stride;
+    const int j0 = (Hq + Hkv) * D + hk * D;
+    vo[i] = from_f32<T>(val(j0 + i));
+    vo[i + half] = from_f32<T>(val(j0 + i + half));
+  }
+}
+
 // Families chosen by (N, K) alone (so an output element's k order never depends on M):
 //  * N < 16384 (QKV, O, down projections) with whole-stage quarters of K: plain tiles, one
 //    workgroup per (tile, k-quarter), partials added by gemm_reduce_kernel;
@@ -285,14 +347,26 @@ bool quarter_split(int N, int K, int dtype) {
   return N < kWideN && K % (4 * bk) == 0;
 }
 
-template <typename T, typename OutT, typename Cfg>
+// The four k-quarter partial tiles of a [M, N] product into P; the tile height follows M only.
+template <typename T, typename Cfg>
+void launch_quarter_cfg(int M, int N, int K, const void* a, const void* w, float* P, hipStream_t st) {
+  const int mtiles = (M + Cfg::BM - 1) / Cfg::BM, ntiles = (N + Cfg::BN - 1) / Cfg::BN;
+  allow_lds(gemm_quarter_kernel<T, Cfg>, Cfg::RING);
+  hipLaunchKernelGGL((gemm_quarter_kernel<T, Cfg>), dim3(4 * mtiles * ntiles), dim3(Cfg::NT), Cfg::RING, st,
+                     reinterpret_cast<const T*>(a), reinterpret_cast<const T*>(w), P, M, N, K);
+}
+
+template <typename T>
+void launch_quarter_tiles(int M, int N, int K, const void* a, const void* w, float* P, hipStream_t st) {
+  if (M <= 32) launch_quarter_cfg<T, PlainSmall<T>>(M, N, K, a, w, P, st);
+  else if (M <= 64) launch_quarter_cfg<T, PlainMid<T>>(M, N, K, a, w, P, st);
+  else launch_quarter_cfg<T, PlainBig<T>>(M, N, K, a, w, P, st);
+}
+
+template <typename T, typename OutT>
 int32_t launch_quarters(int M, int N, int K, int epi, const void* a, const void* w, const void* res, void* c,
                         float* P, hipStream_t st) {
-  const int mtiles = (M + Cfg::BM - 1) / Cfg::BM, ntiles = (N + Cfg::BN - 1) / Cfg::BN;
-  const size_t lds = Cfg::RING;
-  allow_lds(gemm_quarter_kernel<T, Cfg>, lds);
-  hipLaunchKernelGGL((gemm_quarter_kernel<T, Cfg>), dim3(4 * mtiles * ntiles), dim3(Cfg::NT), lds, st,
-                     reinterpret_cast<const T*>(a), reinterpret_cast<const T*>(w), P, M, N, K);
+  launch_quarter_tiles<T>(M, N, K, a, w, P, st);
   const OutT* R = reinterpret_cast<const OutT*>(res);
   OutT* C = reinterpret_cast<OutT*>(c);
   const size_t outs = (size_t)M * (epi == ORTHRUS_EPI_SWIGLU ? N / 2 : N);
@@ -320,11 +394,7 @@ int32_t launch(int M, int N, int K, int epi, const void* a, const void* w, const
                hipStream_t st) {
   constexpr int BK = 8 * (16 / (int)sizeof(T));  // k per 128-byte stage
   if (N < kWideN) {
-    if (K % (4 * BK) == 0) {
-      if (M <= 32) return launch_quarters<T, OutT, PlainSmall<T>>(M, N, K, epi, a, w, res, c, P, st);
-      if (M <= 64) return launch_quarters<T, OutT, PlainMid<T>>(M, N, K, epi, a, w, res, c, P, st);
-      return launch_quarters<T, OutT, PlainBig<T>>(M, N, K, epi, a, w, res, c, P, st);
-    }
+    if (K % (4 * BK) == 0) return launch_quarters<T, OutT>(M, N, K, epi, a, w, res, c, P, st);
     if (M <= 32) return launch_cfg<T, OutT, KsSmall<T>>(M, N, K, epi, a, w, res, c, st);
     return launch_cfg<T, OutT, KsBig<T>>(M, N, K, epi, a, w, res, c, st);
   }
@@ -346,25 +416,7 @@ bool fused_norm_ok(int N, int K, int dtype, const void* x, const void* y) {
 template <typename T>
 int32_t launch_residual_rmsnorm(int M, int N, int K, const void* a, const void* w, void* x, const float* gain,
                                 float eps, void* y, float* P, hipStream_t st) {
-  using Cfg = PlainBig<T>;
-  if (M <= 32) {
-    using C = PlainSmall<T>;
-    const int nt = (N + C::BN - 1) / C::BN, mt = (M + C::BM - 1) / C::BM;
-    allow_lds(gemm_quarter_kernel<T, C>, C::RING);
-    hipLaunchKernelGGL((gemm_quarter_kernel<T, C>), dim3(4 * mt * nt), dim3(C::NT), C::RING, st,
-                       reinterpret_cast<const T*>(a), reinterpret_cast<const T*>(w), P, M, N, K);
-  } else if (M <= 64) {
-    using C = PlainMid<T>;
-    const int nt = (N + C::BN - 1) / C::BN, mt = (M + C::BM - 1) / C::BM;
-    allow_lds(gemm_quarter_kernel<T, C>, C::RING);
-    hipLaunchKernelGGL((gemm_quarter_kernel<T, C>), dim3(4 * mt * nt), dim3(C::NT), C::RING, st,
-                       reinterpret_cast<const T*>(a), reinterpret_cast<const T*>(w), P, M, N, K);
-  } else {
-    const int nt = (N + Cfg::BN - 1) / Cfg::BN, mt = (M + Cfg::BM - 1) / Cfg::BM;
-    allow_lds(gemm_quarter_kernel<T, Cfg>, Cfg::RING);
-    hipLaunchKernelGGL((gemm_quarter_kernel<T, Cfg>), dim3(4 * mt * nt), dim3(Cfg::NT), Cfg::RING, st,
-                       reinterpret_cast<const T*>(a), reinterpret_cast<const T*>(w), P, M, N, K);
-  }
+  launch_quarter_tiles<T>(M, N, K, a, w, P, st);
   hipLaunchKernelGGL(gemm_reduce_rmsnorm_kernel<T>, dim3(M), dim3(256), 0, st, P, reinterpret_cast<T*>(x), gain, eps,
                      M, N, reinterpret_cast<T*>(y));
   return check_launch("orthrus_gemm_residual_rmsnorm");
@@ -445,6 +497,50 @@ extern "C" int32_t orthrus_gemm_residual_rmsnorm(int32_t M, int32_t N, int32_t K
                                stream))
     return s;
   return orthrus_rmsnorm(M, N, dtype, x, gain, eps, y, stream);
+}
+
+extern "C" int32_t orthrus_gemm_rope_kv_write(int32_t batch, int32_t block, int32_t q_heads, int32_t kv_heads,
+                                              int32_t head_dim, int32_t page_size, int32_t max_pages, int32_t hidden,
+                                              int32_t dtype, const void* a, const void* w, const float* rope_table,
+                                              int32_t max_pos, const int32_t* ctx_len, const int32_t* page_table,
+                                              void* qkv, void* q_out, void* k_dst, void* v_dst, void* workspace,
+                                              size_t workspace_bytes, void* stream) {
+  ORTHRUS_REQUIRE(batch >= 0 && block >= 1 && q_heads > 0 && kv_heads > 0 && head_dim > 0 && head_dim % 2 == 0,
+                  ORTHRUS_ERR_INVALID_ARG, "gemm_rope_kv_write: bad sizes");
+  const int M = batch * block, N = (q_heads + 2 * kv_heads) * head_dim, K = hidden;
+  if (int32_t s = validate(M, N, K, dtype, dtype, ORTHRUS_EPI_STORE)) return s;
+  ORTHRUS_REQUIRE(a && w && rope_table && ctx_len && qkv && q_out && k_dst && v_dst && max_pos > 0,
+                  ORTHRUS_ERR_INVALID_ARG, "gemm_rope_kv_write: bad args");
+  ORTHRUS_REQUIRE(!page_table || (page_size > 0 && max_pages > 0), ORTHRUS_ERR_INVALID_ARG,
+                  "gemm_rope_kv_write: paging");
+  if (batch == 0) return ORTHRUS_OK;
+  const size_t need = orthrus_gemm_workspace_bytes(M, N, K, dtype, ORTHRUS_EPI_STORE);
+  ORTHRUS_REQUIRE(need == 0 || (workspace && workspace_bytes >= need), ORTHRUS_ERR_WORKSPACE,
+                  "gemm_rope_kv_write: workspace %zu < %zu bytes", workspace ? workspace_bytes : (size_t)0, need);
+  ORTHRUS_REQUIRE(need == 0 || ((uintptr_t)workspace & 15) == 0, ORTHRUS_ERR_INVALID_ARG,
+                  "gemm_rope_kv_write: workspace not 16-byte aligned");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (!quarter_split(N, K, dtype) || head_dim > 512 || 256 % (head_dim / 2) != 0) {
+    // other shapes: the two calls in sequence through qkv (the fused pass has their bits)
+    if (int32_t s = orthrus_gemm(M, N, K, dtype, dtype, ORTHRUS_EPI_STORE, a, w, nullptr, qkv, workspace,
+                                 workspace_bytes, stream))
+      return s;
+    return orthrus_rope_kv_write(batch, block, q_heads, kv_heads, head_dim, page_size, max_pages, dtype, qkv,
+                                 rope_table, max_pos, ctx_len, page_table, q_out, k_dst, v_dst, stream);
+  }
+  float* P = reinterpret_cast<float*>(workspace);
+  auto quarters = [&](auto tag) {
+    using T = decltype(tag);
+    launch_quarter_tiles<T>(M, N, K, a, w, P, st);
+    const int hpw = 256 / (head_dim / 2);
+    hipLaunchKernelGGL(gemm_reduce_rope_kv_kernel<T>, dim3(M, (q_heads + 2 * kv_heads + hpw - 1) / hpw), dim3(256), 0,
+                       st, P, M, rope_table, max_pos, ctx_len,
+                       page_table, block, q_heads, kv_heads, head_dim, page_size, max_pages, reinterpret_cast<T*>(q_out),
+                       reinterpret_cast<T*>(k_dst), reinterpret_cast<T*>(v_dst));
+  };
+  if (dtype == ORTHRUS_BF16) quarters(bf16{});
+  else quarters(float{});
+  return check_launch("orthrus_gemm_rope_kv_write");
 }
 
 extern "C" int32_t orthrus_pack_gate_up(int32_t inter, int32_t hidden, int32_t dtype, const void* gate,

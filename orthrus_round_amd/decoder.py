@@ -164,15 +164,16 @@ class Decoder:
         L.rmsnorm(M, H, dt, x, self.layers[0]["attn_norm"], s.eps, a)
         for l, Wl in enumerate(self.layers):
             nxt = self.layers[l + 1]["attn_norm"] if l + 1 < len(self.layers) else self.final_norm
-            L.gemm(M, self.nqkv, H, dt, dt, L.EPI_STORE, a, Wl["qkv_" + view], None, self.qkv, self.gemm_ws)
             if draft:
-                L.rope_kv_write(nb, kb, Hq, Hkv, D, self.page, self.max_pages, dt, self.qkv, self.rope,
-                                self.max_pos, ctx, None, self.q, self.k_blk, self.v_blk)
+                L.gemm_rope_kv_write(nb, kb, Hq, Hkv, D, self.page, self.max_pages, H, dt, a, Wl["qkv_" + view],
+                                     self.rope, self.max_pos, ctx, None, self.qkv, self.q, self.k_blk, self.v_blk,
+                                     self.gemm_ws)
                 L.draft_attn(desc, self.q, self.k_pages[l], self.v_pages[l], self.page_table, ctx, self.k_blk,
                              self.v_blk, self.o, ws)
             else:
-                L.rope_kv_write(nb, kb, Hq, Hkv, D, self.page, self.max_pages, dt, self.qkv, self.rope,
-                                self.max_pos, ctx, self.page_table, self.q, self.k_pages[l], self.v_pages[l])
+                L.gemm_rope_kv_write(nb, kb, Hq, Hkv, D, self.page, self.max_pages, H, dt, a, Wl["qkv_" + view],
+                                     self.rope, self.max_pos, ctx, self.page_table, self.qkv, self.q,
+                                     self.k_pages[l], self.v_pages[l], self.gemm_ws)
                 L.verify_attn(desc, self.q, self.k_pages[l], self.v_pages[l], self.page_table, ctx, self.o, ws)
             L.gemm_residual_rmsnorm(M, H, Hq * D, dt, self.o, Wl["o_" + view], x, Wl["mlp_norm"], s.eps, a,
                                     self.gemm_ws)

@@ -465,3 +465,38 @@ def test_gemm_residual_rmsnorm_has_the_bits_of_the_two_calls(dtype, M, N, K):
     ref = z / np.sqrt((z ** 2).mean(1, keepdims=True) + 1e-6) * gain.cpu().numpy()
     out = yf.float().cpu().numpy()
     assert np.abs(out - ref).max() / np.abs(ref).max() <= (2e-2 if bf else 1e-5)
+
+
+@pytest.mark.parametrize("dtype", [ora.BF16, ora.F32])
+@pytest.mark.parametrize("paged", [True, False])
+@pytest.mark.parametrize("B,H", [(8, 4096), (2, 512), (3, 192)])
+def test_gemm_rope_kv_write_has_the_bits_of_the_two_calls(dtype, paged, B, H):
+    """The fused QKV projection + RoPE + K/V write (row by row from the k-quarter partials where the
+    GEMM splits K, the two calls through qkv otherwise) gives exactly the bits of orthrus_gemm(STORE)
+    followed by orthrus_rope_kv_write: q, the written K/V slots, and untouched slots left as they were."""
+    K, Hq, Hkv, D, page = 32, 8, 2, 128, 16
+    bf = dtype == ora.BF16
+    tdt = torch.bfloat16 if bf else torch.float32
+    N = (Hq + 2 * Hkv) * D
+    a, w = synth.lmhead_inputs(30, B * K, H, N, h_std=1.0, w_std=0.05, bf16=bf)
+    ctx = (np.arange(B, dtype=np.int32) * 611) % 3000
+    maxpos = 4096
+    table = torch.empty((maxpos, D // 2, 2), dtype=torch.float32, device=DEV)
+    ora.rope_table(maxpos, D, 1e6, table)
+    maxp = (3000 + K) // page + 1
+    pt = dev(np.random.default_rng(1).permutation(B * maxp).astype(np.int32).reshape(B, maxp)) if paged else None
+    ws = gemm_ws(B * K, N, H, dtype, ora.EPI_STORE)
+
+    def dests():
+        shape = (B * maxp, Hkv, page, D) if paged else (B, K, Hkv, D)
+        return (torch.empty((B * K, Hq * D), dtype=tdt, device=DEV), torch.full(shape, 7.0, dtype=tdt, device=DEV),
+                torch.full(shape, 7.0, dtype=tdt, device=DEV))
+    qs, ks, vs = dests()
+    qkv = torch.empty((B * K, N), dtype=tdt, device=DEV)
+    ora.gemm(B * K, N, H, dtype, dtype, ora.EPI_STORE, dev(a, dtype), dev(w, dtype), None, qkv, ws)
+    ora.rope_kv_write(B, K, Hq, Hkv, D, page, maxp, dtype, qkv, table, maxpos, dev(ctx), pt, qs, ks, vs)
+    qf, kf, vf = dests()
+    ora.gemm_rope_kv_write(B, K, Hq, Hkv, D, page, maxp, H, dtype, dev(a, dtype), dev(w, dtype), table, maxpos,
+                           dev(ctx), pt, torch.empty_like(qkv), qf, kf, vf, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(qs, qf) and torch.equal(ks, kf) and torch.equal(vs, vf)
