@@ -440,20 +440,48 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   if (r >= K) return;
   const size_t row0 = ((size_t)(b * a.Hkv + hk) * a.nchunk_max * G + w) * 32 + r;
   const size_t cstride = (size_t)G * 32;
+  // several chunks' loads are kept in flight at once; the additions still run in chunk order
   float M = kNegInf;
+#pragma unroll 8
   for (int c = 0; c < nchunks; ++c) M = fmaxf(M, a.part_ml[(row0 + c * cstride) * 2]);
   constexpr int NV = D / (4 * TPR);
   f32x4 acc[NV];
 #pragma unroll
   for (int j = 0; j < NV; ++j) acc[j] = f32x4{0, 0, 0, 0};
   float lsum = 0.0f;
-  for (int c = 0; c < nchunks; ++c) {
-    const size_t row = row0 + c * cstride;
-    const float wc = exp2f(a.part_ml[row * 2] - M);
-    lsum += wc * a.part_ml[row * 2 + 1];
-    const float* pa = a.part_acc + row * D;
+  auto add = [&](float m, float l, const f32x4 (&x)[NV]) {
+    const float wc = exp2f(m - M);
+    lsum += wc * l;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) acc[j] += wc * *reinterpret_cast<const f32x4*>(pa + (j * TPR + part) * 4);
+    for (int j = 0; j < NV; ++j) acc[j] += wc * x[j];
+  };
+  // four chunks' partials are loaded into separate registers before they are added in order
+  constexpr int U = 4;
+  int c = 0;
+  for (; c + U <= nchunks; c += U) {
+    float m[U], l[U];
+    f32x4 x[U][NV];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t row = row0 + (c + u) * cstride;
+      m[u] = a.part_ml[row * 2];
+      l[u] = a.part_ml[row * 2 + 1];
+      const float* pa = a.part_acc + row * D;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) x[u][j] = *reinterpret_cast<const f32x4*>(pa + (j * TPR + part) * 4);
+    }
+    // keep the scheduler from sinking each load next to its use, which would serialise them again
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) add(m[u], l[u], x[u]);
+  }
+  for (; c < nchunks; ++c) {
+    const size_t row = row0 + c * cstride;
+    const float* pa = a.part_acc + row * D;
+    f32x4 x[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) x[j] = *reinterpret_cast<const f32x4*>(pa + (j * TPR + part) * 4);
+    add(a.part_ml[row * 2], a.part_ml[row * 2 + 1], x);
   }
   OutT* orow = reinterpret_cast<OutT*>(a.out) + ((size_t)(b * K + r) * a.Hq + hk * G + w) * D;
 #pragma unroll
