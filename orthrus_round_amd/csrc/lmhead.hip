@@ -120,15 +120,32 @@ __global__ __launch_bounds__(64) void lmhead_finalize(const uint64_t* part_best,
   const int row = blockIdx.x, lane = threadIdx.x;
   uint64_t best = 0;
   float lm = -__builtin_huge_valf(), ls = 0.0f;
-  for (int t = lane; t < ntiles; t += 64) {
-    const size_t o = (size_t)row * ntiles + t;
-    best = umax64(best, part_best[o]);
-    const float m2 = part_m[o];
+  auto merge = [&](uint64_t b2, float m2, float s2) {
+    best = umax64(best, b2);
     if (m2 != -__builtin_huge_valf()) {
-      if (lm == -__builtin_huge_valf()) { lm = m2; ls = part_s[o]; }
-      else lse_merge(lm, ls, m2, part_s[o]);
+      if (lm == -__builtin_huge_valf()) { lm = m2; ls = s2; }
+      else lse_merge(lm, ls, m2, s2);
     }
+  };
+  // four of the lane's tiles are loaded before they are merged in tile order
+  constexpr int U = 4;
+  const size_t base = (size_t)row * ntiles;
+  int t = lane;
+  for (; t + 64 * (U - 1) < ntiles; t += 64 * U) {
+    uint64_t b2[U];
+    float m2[U], s2[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t o = base + t + 64 * u;
+      b2[u] = part_best[o];
+      m2[u] = part_m[o];
+      s2[u] = part_s[o];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) merge(b2[u], m2[u], s2[u]);
   }
+  for (; t < ntiles; t += 64) merge(part_best[base + t], part_m[base + t], part_s[base + t]);
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     best = umax64(best, shfl_xor_u64(best, off));
