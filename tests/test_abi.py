@@ -45,6 +45,16 @@ def test_struct_layouts_match_header():
     (lambda: ora.gemm(4, 64, 64, ora.BF16, ora.BF16, 1, 1, 1, None, 1, stream=0), 1),
     (lambda: ora.gemm(4, 64, 64, ora.F32, ora.BF16, 0, 1, 1, None, 1, stream=0), 2),
     (lambda: ora.gemm(4, 64, 256, ora.BF16, ora.BF16, 0, 1, 1, None, 1, stream=0), 3),  # no workspace
+    (lambda: ora.gemm(4, 64, 256, ora.BF16, ora.BF16, 0, 1, 1, None, 1, ws=17, stream=0), 3),  # 0 bytes given
+    (lambda: ora.gemm_residual_rmsnorm(4, 64, 256, ora.BF16, 1, 1, 1, 1, 1e-6, 1, stream=0), 3),
+    (lambda: ora.gemm_residual_rmsnorm(4, 64, 96, ora.BF16, 1, 1, 1, 1, 1e-6, 1, stream=0), 2),  # K % 64
+    (lambda: ora.gemm_residual_rmsnorm(4, 64, 64, ora.BF16, 1, 1, 1, None, 1e-6, 1, stream=0), 1),  # no gain
+    (lambda: ora.gemm_rope_kv_write(1, 32, 8, 2, 128, 16, 4, 4096, ora.BF16, 1, 1, 1, 64, 1, None, 1, 1, 1, 1,
+                                    stream=0), 3),  # no workspace
+    (lambda: ora.gemm_rope_kv_write(1, 32, 8, 2, 127, 16, 4, 4096, ora.BF16, 1, 1, 1, 64, 1, None, 1, 1, 1, 1,
+                                    stream=0), 1),  # odd head_dim
+    (lambda: ora.gemm_rope_kv_write(1, 0, 8, 2, 128, 16, 4, 4096, ora.BF16, 1, 1, 1, 64, 1, None, 1, 1, 1, 1,
+                                    stream=0), 1),  # empty block
     (lambda: ora.consensus_commit(2, 33, 1, 1, 1, 1, 1, 1, 1, 1, 1, 8, 64, stream=0), 1),
     (lambda: ora.rmsnorm(2, 64, 7, 1, 1, 1e-6, 1, stream=0), 1),
     (lambda: ora.rope_table(0, 64, 1e6, 1, stream=0), 1),
