@@ -25,7 +25,10 @@ Readings where the pages are silent (each listed in the design notes):
   d_1..d_K and the verify rows are [anchor, d_1 .. d_{K-1}];
 * full acceptance commits K tokens (no bonus token); the context grows by min(k+1, K);
 * the initial state prefills prompt[:-1] and takes prompt[-1] as the first anchor;
-* [MASK] is the reserved id V-1.
+* [MASK] is the reserved id V-1;
+* two-step drafting (the sec. 六 ablation): pass 1 fills half of the K-1 masked slots, rounded
+  down, choosing its most confident predictions (log-probability of the argmax; equal values to
+  the lower slot); pass 2 re-predicts the rest, and a filled slot keeps its pass-1 token.
 """
 from __future__ import annotations
 
@@ -146,6 +149,51 @@ def gumbel_sample(z: np.ndarray, temperature: float, u: np.ndarray) -> int:
     return int(np.argmax(zt + g.astype(z.dtype)))
 
 
+def log_confidence(z: np.ndarray, tok) -> np.ndarray:
+    """Per row, the log-probability of the row's chosen token under softmax(z):
+    z[i, tok_i] - logsumexp_x z[i, x]."""
+    z = np.asarray(z, dtype=np.float64)
+    tok = np.asarray(tok, dtype=np.int64)
+    m = z.max(axis=1)
+    lse = m + np.log(np.exp(z - m[:, None]).sum(axis=1))
+    return z[np.arange(len(tok)), tok] - lse
+
+
+def most_confident(conf, n_fill: int) -> np.ndarray:
+    """Boolean mask of the ``n_fill`` largest entries of ``conf``.  Equal values are taken in
+    index order; a NaN counts as -inf."""
+    c = np.where(np.isnan(conf), -np.inf, np.asarray(conf, dtype=np.float64))
+    order = sorted(range(len(c)), key=lambda i: (-c[i], i))
+    sel = np.zeros(len(c), dtype=bool)
+    sel[order[:n_fill]] = True
+    return sel
+
+
+def two_step_draft(Wt: M.Weights, cache: Cache, anchor: int, block: int, n_fill: int | None = None,
+                   rowwise: bool = True):
+    """Two-step drafting, the Fast-dLLM-v2 style variant that Orthrus paper summary sec. 六
+    ablates (the diffusion view completes the block in two passes instead of one).
+
+    Pass 1 runs over [anchor, MASK x (K-1)].  Its predictions for the K-1 masked slots (row j
+    predicts slot j+1) are ranked by their log-probability; the ``n_fill`` most confident are
+    written into their slots (default: half of the masks, rounded down) and pass 2 runs over
+    that block.  A filled slot keeps its pass-1 token; every other row takes pass 2's choice.
+    Returns (drafts, d1, d2, filled) with filled[j] true when row j's token came from pass 1.
+    """
+    K = block
+    mask = Wt.shape.mask_id
+    if n_fill is None:
+        n_fill = (K - 1) // 2
+    z1 = draft_pass(Wt, cache, [anchor] + [mask] * (K - 1), rowwise)
+    d1 = M.argmax_lowest(z1)
+    filled = np.zeros(K, dtype=bool)
+    filled[: K - 1] = most_confident(log_confidence(z1[: K - 1], d1[: K - 1]), n_fill)
+    blk2 = [anchor] + [int(d1[j]) if filled[j] else mask for j in range(K - 1)]
+    z2 = draft_pass(Wt, cache, blk2, rowwise)
+    d2 = M.argmax_lowest(z2)
+    return np.where(filled, d1, d2).astype(np.int32), d1, d2, filled
+
+
 @dataclasses.dataclass
 class RoundLog:
     n_before: int
@@ -178,7 +226,8 @@ def prefill(Wt: M.Weights, prompt, capacity: int, rowwise: bool = True):
 
 def generate(Wt: M.Weights, prompt, max_new: int, block: int = 32, temperature: float = 0.0,
              seed: int = 0, seq_id: int = 0, rowwise: bool = True, inject=None,
-             poison_dead: bool = False, max_rounds: int | None = None) -> GenResult:
+             poison_dead: bool = False, max_rounds: int | None = None,
+             two_step: int | None = None) -> GenResult:
     """Orthrus decoding of one sequence.
 
     ``inject`` (optional callable round, n, anchor -> drafts[K]) replaces the diffusion
@@ -186,7 +235,10 @@ def generate(Wt: M.Weights, prompt, max_new: int, block: int = 32, temperature: 
     beyond the committed length with NaN after each round (rollback must make them
     unreachable).  At temperature > 0 drafts are sampled from the diffusion view with the
     DRAFT stream, accepted with the ACCEPT stream and corrected with the RESID stream.
+    ``two_step`` (greedy only) drafts with ``two_step_draft`` filling that many masks, which
+    costs one more forward pass per round.
     """
+    assert two_step is None or temperature == 0.0
     shape = Wt.shape
     K = block
     cache, anchor = prefill(Wt, prompt, len(prompt) + max_new + 2 * K, rowwise)
@@ -195,10 +247,14 @@ def generate(Wt: M.Weights, prompt, max_new: int, block: int = 32, temperature: 
     while len(out) < max_new and (max_rounds is None or r < max_rounds):
         n = cache.n
         blk = [anchor] + [shape.mask_id] * (K - 1)
-        zd = draft_pass(Wt, cache, blk, rowwise)
-        if temperature == 0.0:
+        if two_step is not None:
+            d = two_step_draft(Wt, cache, anchor, K, two_step, rowwise)[0]
+            passes += 1
+        elif temperature == 0.0:
+            zd = draft_pass(Wt, cache, blk, rowwise)
             d = M.argmax_lowest(zd)
         else:
+            zd = draft_pass(Wt, cache, blk, rowwise)
             d = np.array([gumbel_sample(zd[i], temperature,
                                         uniforms(seed, STREAM_DRAFT, i, np.arange(shape.vocab), r, seq_id))
                           for i in range(K)], dtype=np.int32)

@@ -397,3 +397,75 @@ def test_tiny_config_full_256_tokens(tiny, tiny_prompt):
     res = Dc.generate(Wt, tiny_prompt, 256)
     assert res.tokens == Dc.generate_ar(Wt, tiny_prompt, 256)
     assert min(len(r.emitted) for r in res.rounds) >= 1
+
+
+# --------------------------------------------------------------------------- two-step drafting
+
+def test_log_confidence_closed_form_and_normalisation():
+    # softmax([0, ln 3]) = (1/4, 3/4)
+    z = np.array([[0.0, np.log(3.0)], [5.0, 5.0 + np.log(3.0)]])
+    assert np.allclose(Dc.log_confidence(z, [1, 0]), [np.log(0.75), np.log(0.25)], rtol=0, atol=1e-15)
+    rs = np.random.default_rng(0)
+    z = rs.standard_normal((4, 50)) * 3.0 + 700.0  # large offset: a naive exp would overflow
+    for x in range(50):
+        assert np.isfinite(Dc.log_confidence(z, [x] * 4)).all()
+    total = sum(np.exp(Dc.log_confidence(z, [x] * 4)) for x in range(50))
+    assert np.allclose(total, 1.0, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_most_confident_is_the_unique_ordered_subset(seed):
+    import itertools
+    rs = np.random.default_rng(seed)
+    c = rs.integers(0, 4, 7).astype(np.float64)  # many ties
+    if seed % 2:
+        c[rs.integers(0, 7)] = np.nan
+    key = np.where(np.isnan(c), -np.inf, c)
+    for n_fill in range(8):
+        ok = []
+        for S in itertools.combinations(range(7), n_fill):
+            rest = [j for j in range(7) if j not in S]
+            if all(key[i] > key[j] or (key[i] == key[j] and i < j) for i in S for j in rest):
+                ok.append(set(S))
+        assert len(ok) == 1
+        assert set(np.flatnonzero(Dc.most_confident(c, n_fill))) == ok[0]
+
+
+@pytest.fixture(scope="module")
+def tiny_cache(tiny, tiny_prompt):
+    shape, W, Wt = tiny
+    cache, anchor = Dc.prefill(Wt, tiny_prompt, 160)
+    return cache, anchor
+
+
+def test_two_step_with_no_fill_is_the_one_step_draft(tiny, tiny_cache):
+    shape, W, Wt = tiny
+    cache, anchor = tiny_cache
+    d, d1, d2, filled = Dc.two_step_draft(Wt, cache, anchor, 32, n_fill=0)
+    one = M.argmax_lowest(Dc.draft_pass(Wt, cache, [anchor] + [shape.mask_id] * 31))
+    assert not filled.any() and np.array_equal(d, one) and np.array_equal(d1, one) and np.array_equal(d2, one)
+
+
+def test_two_step_fills_half_and_keeps_pass_one_tokens(tiny, tiny_cache):
+    shape, W, Wt = tiny
+    cache, anchor = tiny_cache
+    d, d1, d2, filled = Dc.two_step_draft(Wt, cache, anchor, 32)
+    assert filled.sum() == 15 and not filled[31]
+    assert np.array_equal(d[filled], d1[filled]) and np.array_equal(d[~filled], d2[~filled])
+    # the filled rows are the most confident pass-1 rows
+    conf = Dc.log_confidence(Dc.draft_pass(Wt, cache, [anchor] + [shape.mask_id] * 31)[:31], d1[:31])
+    assert conf[filled[:31]].min() >= conf[~filled[:31]].max()
+    # pass 2 sees the filled tokens: with every mask filled, pass 2's block is the verify block
+    # of a one-step round with drafts d1, and only the last row comes from pass 2
+    d, d1, d2, filled = Dc.two_step_draft(Wt, cache, anchor, 32, n_fill=31)
+    assert filled[:31].all() and np.array_equal(d[:31], d1[:31]) and d[31] == d2[31]
+    verify_block = [anchor] + [int(t) for t in d1[:31]]  # slot j holds row j-1's token, as in verify
+    assert np.array_equal(d2, M.argmax_lowest(Dc.draft_pass(Wt, cache, verify_block)))
+
+
+def test_two_step_orthrus_equals_greedy_ar(tiny, tiny_prompt):
+    shape, W, Wt = tiny
+    res = Dc.generate(Wt, tiny_prompt, 40, two_step=15)
+    assert res.tokens == Dc.generate_ar(Wt, tiny_prompt, 40)
+    assert res.passes == 3 * len(res.rounds)
+    assert all(1 <= len(r.emitted) <= 32 for r in res.rounds)
