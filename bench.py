@@ -289,6 +289,33 @@ def block_sweep(dec, prompts, blocks=(4, 8, 16, 32), rounds=12):
     return res
 
 
+def two_step_drafting(dec, prompts, n_fill=15, rounds=12, n_tokens=32):
+    """Two-step drafting (the variant the pages ablate): round latency by graph replay, committed
+    tokens per round and per forward pass (three passes a round), and whether the committed
+    trajectory still equals AR decoding.  With random weights the acceptance says nothing about
+    the trained model; the latency and the losslessness do."""
+    import torch
+    B = len(prompts)
+    dec.prefill(torch.from_numpy(prompts), max_out=32 * (rounds + 4))
+    g = dec.capture(dec.round_greedy_two_step, n_fill)
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    out0 = int(dec.out_len.sum())
+    t0 = time.perf_counter()
+    for _ in range(rounds):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / rounds * 1e3
+    per_round = (int(dec.out_len.sum()) - out0) / (rounds * B)
+    del g
+    a, _ = dec.generate(prompts, n_tokens, two_step=n_fill, use_graph=True)
+    b, _ = dec.generate_ar(prompts, n_tokens, use_graph=True)
+    return {"n_fill": n_fill, "round_ms": round(ms, 4), "tokens_per_round_per_seq": round(per_round, 4),
+            "tpf": round(per_round / 3, 4), "trajectory_equals_ar": bool(np.array_equal(a, b)),
+            "match_tokens": n_tokens}
+
+
 def trajectory_match(dec, W, shape, prompts, n_tokens, kv_chunk):
     """Greedy Orthrus vs greedy AR through the same kernels: fraction of sequences whose first
     n_tokens agree exactly, in bf16 (the timed decoder) and fp32 (the same bf16-valued weights
@@ -466,9 +493,10 @@ def main():
     torch.cuda.synchronize()
     ar_ms = (time.perf_counter() - ta) / 20 * 1e3
 
-    sweep = match = control = memory = None
+    sweep = match = control = memory = two = None
     if not args.no_extras:
         sweep = block_sweep(dec, prompts)
+        two = two_step_drafting(dec, prompts)
         match = trajectory_match(dec, W, shape, prompts, args.match_tokens, args.kv_chunk)
         control = divergence_control(dec, prompts, args.match_tokens, args.kv_chunk, args.control_chunk)
         memory = memory_overhead(W, shape, args.batch, args.kv_chunk)
@@ -509,6 +537,7 @@ def main():
                         "GBs": round(v["bytes"] / v["ms"] / 1e6, 1)} for k, v in tab.items()},
         "attention_roofline": attn,
         "round_ms_by_block": sweep,
+        "two_step_drafting": two,
         "trajectory_match_vs_ar": match,
         "divergence_control_bf16": control,
         "memory_vs_ar": memory,

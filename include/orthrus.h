@@ -264,6 +264,36 @@ int32_t orthrus_embed_block(int32_t batch, int32_t block, int32_t hidden, int32_
                             int32_t tok_stride, int32_t tok_offset, int32_t mask_id, void* x,
                             void* stream);
 
+/* ------------------------------------------------------------------------------------------
+ * Two-step drafting (Orthrus paper summary, sec. 六: the ablation that borrows Fast-dLLM-v2's
+ * two-pass completion; the diffusion view fills the block in two passes instead of one).
+ *
+ * orthrus_draft_fill, between the two diffusion passes:
+ *   h [batch*block, hidden] (dtype): pass 1's final-normed hidden rows (the LM head's input);
+ *   w [vocab, hidden] (dtype): the LM-head weight; lse [batch*block] fp32: logsumexp of pass 1's
+ *   logits (orthrus_lmhead_argmax's lse_out at temperature 0); draft [batch, block]: pass 1's
+ *   argmax, row j being the token for slot j+1.
+ *   For each sequence, rows j < block-1 are scored by z[j, draft_j] - lse_j (the chosen token's
+ *   log-probability; z recomputed in fp32 as one dot product; a NaN score counts as -inf) and
+ *   the n_fill best (equal scores: lower j first) are filled:
+ *     tokens2[b, j] = filled ? draft[b, j] : mask_id, filled[b, j] = 1 or 0, for j < block-1;
+ *     tokens2[b, block-1] = mask_id, filled[b, block-1] = 0.
+ *   tokens2 is the token list of pass 2's block after the anchor (orthrus_embed_block with
+ *   tokens = tokens2, tok_stride = block, tok_offset = 0).
+ *   Supported: 1 <= block <= 64, 0 <= n_fill <= block-1, dtype bf16 or fp32, hidden % 8 == 0.
+ * orthrus_draft_merge, after pass 2's LM head:
+ *   draft_out[i] = filled[i] ? tokens2[i] : draft2[i] over batch*block entries (a filled slot keeps
+ *   its pass-1 token).  draft_out may alias draft2.
+ * Both return ORTHRUS_ERR_INVALID_ARG for null pointers or sizes out of range before launching.
+ * ------------------------------------------------------------------------------------------ */
+int32_t orthrus_draft_fill(int32_t batch, int32_t block, int32_t hidden, int32_t vocab, int32_t dtype,
+                           const void* h, const void* w, const float* lse, const int32_t* draft,
+                           int32_t mask_id, int32_t n_fill, int32_t* tokens2, int32_t* filled,
+                           void* stream);
+int32_t orthrus_draft_merge(int32_t batch, int32_t block, const int32_t* filled,
+                            const int32_t* tokens2, const int32_t* draft2, int32_t* draft_out,
+                            void* stream);
+
 /* Philox4x64-10 words for n counters (ctr [n, 4], out [n, 4] uint64), key (k0, k1). */
 int32_t orthrus_philox4x64(int64_t n, const uint64_t* ctr, uint64_t k0, uint64_t k1,
                            uint64_t* out, void* stream);

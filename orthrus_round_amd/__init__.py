@@ -7,7 +7,9 @@ calls only.  PyTorch provides device memory and streams.
 """
 from ._lib import (BF16, F32, EPI_RESIDUAL, EPI_STORE, EPI_SWIGLU, STREAM_ACCEPT, STREAM_AR, STREAM_DRAFT,
                    STREAM_RESID, OrthrusError, abi_version, attn_desc, attn_workspace_bytes, consensus_commit,
-                   draft_attn, embed_block, gemm, gemm_residual_rmsnorm, gemm_rope_kv_write, gemm_workspace_bytes, lib, lmhead_argmax, lmhead_desc, lmhead_workspace_bytes,
-                   pack_gate_up, philox4x64, rejection_accept, rmsnorm, rope_kv_write, rope_table, verify_attn)
+                   draft_attn, draft_fill, draft_merge, embed_block, gemm, gemm_residual_rmsnorm,
+                   gemm_rope_kv_write, gemm_workspace_bytes, lib, lmhead_argmax, lmhead_desc,
+                   lmhead_workspace_bytes, pack_gate_up, philox4x64, rejection_accept, rmsnorm, rope_kv_write,
+                   rope_table, verify_attn)
 
 __all__ = [n for n in dir() if not n.startswith("_")]

@@ -53,6 +53,8 @@ _SIGS = {
     "orthrus_lmhead_workspace_bytes": ([ctypes.POINTER(LmHeadDesc)], _SZ),
     "orthrus_lmhead_argmax": ([ctypes.POINTER(LmHeadDesc), _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I32),
     "orthrus_consensus_commit": ([_I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P], _I32),
+    "orthrus_draft_fill": ([_I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _I32, _I32, _P, _P, _P], _I32),
+    "orthrus_draft_merge": ([_I32, _I32, _P, _P, _P, _P, _P], _I32),
     "orthrus_rejection_workspace_bytes": ([_I32], _SZ),
     "orthrus_rejection_accept": ([_I32, _I32, _I32, _F32, _U64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                   _P, _P, _I32, _I32, _P, _SZ, _P], _I32),
@@ -152,6 +154,16 @@ def consensus_commit(batch, block, draft, target, ctx_len, anchor, accept, out_t
     _check(lib().orthrus_consensus_commit(batch, block, _ptr(draft), _ptr(target), _ptr(ctx_len), _ptr(anchor),
                                           _ptr(accept), _ptr(out_tokens), _ptr(out_len), _ptr(round_), _ptr(done),
                                           max_out, max_ctx, _stream(stream)))
+
+
+def draft_fill(batch, block, hidden, vocab, dtype, h, w, lse, draft, mask_id, n_fill, tokens2, filled, stream=None):
+    _check(lib().orthrus_draft_fill(batch, block, hidden, vocab, dtype, _ptr(h), _ptr(w), _ptr(lse), _ptr(draft),
+                                    mask_id, n_fill, _ptr(tokens2), _ptr(filled), _stream(stream)))
+
+
+def draft_merge(batch, block, filled, tokens2, draft2, draft_out, stream=None):
+    _check(lib().orthrus_draft_merge(batch, block, _ptr(filled), _ptr(tokens2), _ptr(draft2), _ptr(draft_out),
+                                     _stream(stream)))
 
 
 def rejection_accept(batch, block, vocab, temperature, seed, seq_id, draft_logits, target_logits, draft_lse,

@@ -160,6 +160,80 @@ int32_t check_state(int batch, int block, const int32_t* ctx_len, const int32_t*
   return ORTHRUS_OK;
 }
 
+
+// Two-step drafting (Orthrus paper summary, sec. 六: the Fast-dLLM-v2 style ablation in which the
+// diffusion view completes a block in two passes).  After pass 1, row j's choice (the token for
+// slot j+1) is scored by its log-probability z[j, d_j] - logsumexp(z[j]); the n_fill best of the
+// K-1 masked slots (equal scores: lower slot first; NaN scores last) are written into their slots
+// for pass 2, the others stay [MASK].  One workgroup per sequence: each wavefront recomputes the
+// chosen logit of its rows as one dot product (16-byte loads, lane-strided, then a butterfly).
+constexpr int kMaxFillBlock = 64;
+constexpr float kNegInfF = -__builtin_huge_valf();
+
+template <typename T>
+__global__ __launch_bounds__(256) void draft_fill_kernel(int K, int hidden, int vocab, const T* __restrict__ h,
+                                                         const T* __restrict__ w, const float* __restrict__ lse,
+                                                         const int32_t* __restrict__ draft, int mask_id, int n_fill,
+                                                         int32_t* tokens2, int32_t* filled) {
+  constexpr int EPC = 16 / (int)sizeof(T);
+  __shared__ float conf[kMaxFillBlock];
+  const int b = blockIdx.x, tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  for (int j = wv; j < K - 1; j += 4) {
+    const size_t row = (size_t)b * K + j;
+    const int tok = draft[row];
+    const bool ok = tok >= 0 && tok < vocab;
+    float acc = 0.0f;
+    if (ok) {
+      const T* hr = h + row * hidden;
+      const T* wr = w + (size_t)tok * hidden;
+      for (int c = lane * EPC; c < hidden; c += 64 * EPC) {
+        if constexpr (EPC == 8) {
+          const bf16x8 x = *reinterpret_cast<const bf16x8*>(hr + c);
+          const bf16x8 y = *reinterpret_cast<const bf16x8*>(wr + c);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)x[e], (float)y[e], acc);
+        } else {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(hr + c);
+          const f32x4 y = *reinterpret_cast<const f32x4*>(wr + c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(x[e], y[e], acc);
+        }
+      }
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) {
+      const float c = ok ? acc - lse[row] : kNegInfF;
+      conf[j] = __builtin_isnan(c) ? kNegInfF : c;
+    }
+  }
+  __syncthreads();
+  if (tid < K) {
+    int32_t t2 = mask_id, f = 0;
+    if (tid < K - 1) {
+      const float c = conf[tid];
+      int rank = 0;
+      for (int i = 0; i < K - 1; ++i) {
+        const float ci = conf[i];
+        rank += (ci > c || (ci == c && i < tid)) ? 1 : 0;
+      }
+      if (rank < n_fill) {
+        t2 = draft[(size_t)b * K + tid];
+        f = 1;
+      }
+    }
+    tokens2[(size_t)b * K + tid] = t2;
+    filled[(size_t)b * K + tid] = f;
+  }
+}
+
+// The two-step draft: a filled slot keeps its pass-1 token, every other row takes pass 2's.
+__global__ __launch_bounds__(256) void draft_merge_kernel(int n, const int32_t* __restrict__ filled,
+                                                          const int32_t* __restrict__ tokens2, const int32_t* draft2,
+                                                          int32_t* out) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) out[i] = filled[i] ? tokens2[i] : draft2[i];
+}
+
 }  // namespace
 }  // namespace orthrus
 
@@ -209,4 +283,41 @@ extern "C" int32_t orthrus_philox4x64(int64_t n, const uint64_t* ctr, uint64_t k
   hipLaunchKernelGGL(philox_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                      reinterpret_cast<hipStream_t>(stream), n, ctr, k0, k1, out);
   return check_launch("orthrus_philox4x64");
+}
+
+extern "C" int32_t orthrus_draft_fill(int32_t batch, int32_t block, int32_t hidden, int32_t vocab, int32_t dtype,
+                                      const void* h, const void* w, const float* lse, const int32_t* draft,
+                                      int32_t mask_id, int32_t n_fill, int32_t* tokens2, int32_t* filled,
+                                      void* stream) {
+  ORTHRUS_REQUIRE(batch >= 0 && block >= 1 && block <= kMaxFillBlock && hidden > 0 && vocab > 0,
+                  ORTHRUS_ERR_INVALID_ARG, "draft_fill: bad sizes (batch %d, block %d, hidden %d, vocab %d)", batch,
+                  block, hidden, vocab);
+  ORTHRUS_REQUIRE(n_fill >= 0 && n_fill <= block - 1, ORTHRUS_ERR_INVALID_ARG,
+                  "draft_fill: n_fill %d outside [0, block - 1]", n_fill);
+  ORTHRUS_REQUIRE(valid_dtype(dtype), ORTHRUS_ERR_UNSUPPORTED, "draft_fill: dtype %d", dtype);
+  ORTHRUS_REQUIRE(hidden % 8 == 0, ORTHRUS_ERR_UNSUPPORTED, "draft_fill: hidden %% 8 != 0");
+  ORTHRUS_REQUIRE(h && w && lse && draft && tokens2 && filled, ORTHRUS_ERR_INVALID_ARG, "draft_fill: null pointer");
+  if (batch == 0) return ORTHRUS_OK;
+  auto st = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == ORTHRUS_BF16)
+    hipLaunchKernelGGL(draft_fill_kernel<bf16>, dim3(batch), dim3(256), 0, st, block, hidden, vocab,
+                       static_cast<const bf16*>(h), static_cast<const bf16*>(w), lse, draft, mask_id, n_fill, tokens2,
+                       filled);
+  else
+    hipLaunchKernelGGL(draft_fill_kernel<float>, dim3(batch), dim3(256), 0, st, block, hidden, vocab,
+                       static_cast<const float*>(h), static_cast<const float*>(w), lse, draft, mask_id, n_fill,
+                       tokens2, filled);
+  return check_launch("orthrus_draft_fill");
+}
+
+extern "C" int32_t orthrus_draft_merge(int32_t batch, int32_t block, const int32_t* filled, const int32_t* tokens2,
+                                       const int32_t* draft2, int32_t* draft_out, void* stream) {
+  ORTHRUS_REQUIRE(batch >= 0 && block >= 1, ORTHRUS_ERR_INVALID_ARG, "draft_merge: bad sizes");
+  ORTHRUS_REQUIRE(filled && tokens2 && draft2 && draft_out, ORTHRUS_ERR_INVALID_ARG, "draft_merge: null pointer");
+  const int64_t n = (int64_t)batch * block;
+  ORTHRUS_REQUIRE(n < (1ll << 31), ORTHRUS_ERR_INVALID_ARG, "draft_merge: too many rows");
+  if (n == 0) return ORTHRUS_OK;
+  hipLaunchKernelGGL(draft_merge_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), (int)n, filled, tokens2, draft2, draft_out);
+  return check_launch("orthrus_draft_merge");
 }

@@ -128,6 +128,9 @@ class Decoder:
         self.seq_id = torch.arange(self.B, dtype=torch.int32, device=self.dev)
         self.draft = torch.zeros((self.B, block), dtype=torch.int32, device=self.dev)
         self.target = torch.zeros_like(self.draft)
+        # two-step drafting: pass 1's logsumexp, pass 2's block tokens, fill flags, pass 2's choice
+        self.lse1 = torch.empty(M, dtype=torch.float32, device=self.dev)
+        self.tokens2, self.filled, self.draft2 = (torch.zeros_like(self.draft) for _ in range(3))
         self.out_tokens = None
         self.max_out = 0
         self._logits = None
@@ -276,6 +279,28 @@ class Decoder:
         L.consensus_commit(B, K, self.draft, self.target, self.ctx_len, self.anchor, self.accept, self.out_tokens,
                            self.out_len, self.round, self.done, self.max_out, self.max_ctx)
 
+    def round_greedy_two_step(self, n_fill: int):
+        """A greedy round whose draft takes two diffusion passes (two-step drafting): pass 1 over
+        [anchor, MASK...], then its n_fill most confident predictions are written into their slots
+        (orthrus_draft_fill), pass 2 runs over that block, and orthrus_draft_merge keeps the filled
+        tokens.  Verify and consensus are those of the one-pass round."""
+        B, K, s = self.B, self.K, self.shape
+        M = B * K
+        L.embed_block(B, K, s.hidden, self.dt, self.embed, self.anchor, None, 0, 0, s.mask_id, self.x)
+        self._layers("diff", B, K, self.ctx_len, draft=True)
+        self._lm_head(B, K, self.draft, lse=self.lse1[:M])
+        L.draft_fill(B, K, s.hidden, s.vocab, self.dt, self.a[:M], self.lm_head, self.lse1[:M], self.draft, s.mask_id,
+                     n_fill, self.tokens2, self.filled)
+        L.embed_block(B, K, s.hidden, self.dt, self.embed, self.anchor, self.tokens2, K, 0, s.mask_id, self.x)
+        self._layers("diff", B, K, self.ctx_len, draft=True)
+        self._lm_head(B, K, self.draft2)
+        L.draft_merge(B, K, self.filled, self.tokens2, self.draft2, self.draft)
+        L.embed_block(B, K, s.hidden, self.dt, self.embed, self.anchor, self.draft, K, 0, s.mask_id, self.x)
+        self._layers("ar", B, K, self.ctx_len, draft=False)
+        self._lm_head(B, K, self.target)
+        L.consensus_commit(B, K, self.draft, self.target, self.ctx_len, self.anchor, self.accept, self.out_tokens,
+                           self.out_len, self.round, self.done, self.max_out, self.max_ctx)
+
     def round_sampled(self, temperature: float, seed: int):
         B, K, s = self.B, self.K, self.shape
         if self._logits is None:
@@ -321,11 +346,19 @@ class Decoder:
 
     # ------------------------------------------------------------------ drivers
     def generate(self, prompts, max_new: int, temperature: float = 0.0, seed: int = 0, use_graph: bool = False,
-                 poll_every: int = 8, record_accepts: bool = False, max_rounds: int | None = None):
-        """Orthrus decoding; returns (tokens [B, max_new] int32 numpy, GenStats)."""
+                 poll_every: int = 8, record_accepts: bool = False, max_rounds: int | None = None,
+                 two_step: int | None = None):
+        """Orthrus decoding; returns (tokens [B, max_new] int32 numpy, GenStats).  ``two_step``
+        (greedy only) drafts with two diffusion passes, filling that many masks after the first."""
+        assert two_step is None or temperature == 0.0
         self.prefill(torch.as_tensor(prompts), max_new)
         torch.cuda.synchronize(self.dev)
-        fn, args = (self.round_greedy, ()) if temperature == 0.0 else (self.round_sampled, (temperature, seed))
+        if two_step is not None:
+            fn, args = self.round_greedy_two_step, (two_step,)
+        elif temperature == 0.0:
+            fn, args = self.round_greedy, ()
+        else:
+            fn, args = self.round_sampled, (temperature, seed)
         hist = []
         t0 = time.perf_counter()
         if use_graph:
@@ -350,7 +383,8 @@ class Decoder:
         dt = time.perf_counter() - t0
         toks = self.out_tokens.cpu().numpy()
         nround = self.round.cpu().numpy()
-        stats = GenStats(int(nround.max()), int(self.out_len.sum().item()), 2 * int(nround.sum()), dt, hist)
+        passes = (3 if two_step is not None else 2) * int(nround.sum())
+        stats = GenStats(int(nround.max()), int(self.out_len.sum().item()), passes, dt, hist)
         return toks, stats
 
     def generate_ar(self, prompts, max_new: int, temperature: float = 0.0, seed: int = 0, use_graph: bool = False):

@@ -56,6 +56,13 @@ def test_struct_layouts_match_header():
     (lambda: ora.gemm_rope_kv_write(1, 0, 8, 2, 128, 16, 4, 4096, ora.BF16, 1, 1, 1, 64, 1, None, 1, 1, 1, 1,
                                     stream=0), 1),  # empty block
     (lambda: ora.consensus_commit(2, 33, 1, 1, 1, 1, 1, 1, 1, 1, 1, 8, 64, stream=0), 1),
+    (lambda: ora.draft_fill(2, 65, 64, 100, ora.BF16, 1, 1, 1, 1, 99, 3, 1, 1, stream=0), 1),  # block > 64
+    (lambda: ora.draft_fill(2, 32, 64, 100, ora.BF16, 1, 1, 1, 1, 99, 32, 1, 1, stream=0), 1),  # n_fill > 31
+    (lambda: ora.draft_fill(2, 32, 60, 100, ora.BF16, 1, 1, 1, 1, 99, 3, 1, 1, stream=0), 2),  # hidden % 8
+    (lambda: ora.draft_fill(2, 32, 64, 100, 7, 1, 1, 1, 1, 99, 3, 1, 1, stream=0), 2),  # dtype
+    (lambda: ora.draft_fill(2, 32, 64, 100, ora.F32, None, 1, 1, 1, 99, 3, 1, 1, stream=0), 1),
+    (lambda: ora.draft_merge(2, 32, 1, 1, None, 1, stream=0), 1),
+    (lambda: ora.draft_merge(-1, 32, 1, 1, 1, 1, stream=0), 1),
     (lambda: ora.rmsnorm(2, 64, 7, 1, 1, 1e-6, 1, stream=0), 1),
     (lambda: ora.rope_table(0, 64, 1e6, 1, stream=0), 1),
 ])

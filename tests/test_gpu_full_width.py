@@ -81,3 +81,13 @@ def test_orthrus_equals_ar_full_width(weights, prompts, precision):
     b, _ = dec.generate_ar(prompts, 16, use_graph=True)
     assert np.array_equal(a[:, :16], b[:, :16]), [int(np.argmax(a[i, :16] != b[i, :16])) for i in range(8)]
     print(f"{precision}: {st.rounds} rounds for 16 tokens x 8 sequences")
+
+
+def test_two_step_drafting_equals_ar_full_width(weights, prompts):
+    """Two-step drafting (two diffusion passes, 15 masks filled after the first) keeps the round
+    lossless at 8B width in bf16."""
+    dec = Decoder(weights, SHAPE, precision="bf16", block=32, max_batch=8, max_ctx=P + 96, kv_chunk=KV_CHUNK)
+    a, st = dec.generate(prompts, 16, use_graph=True, two_step=15)
+    b, _ = dec.generate_ar(prompts, 16, use_graph=True)
+    assert np.array_equal(a[:, :16], b[:, :16])
+    assert st.passes == 3 * int(dec.round.sum())
