@@ -136,21 +136,29 @@ def kernel_table(dec, ctx_np):
     return tab
 
 
-def source_digest():
-    """sha256 over the kernel sources (orthrus_round_amd/csrc/*, sorted by name)."""
-    import glob
+# The sources each timed kernel is compiled from (orthrus_round_amd/csrc/).
+KERNEL_SOURCES = {
+    "gemm": ("gemm.hip", "gemm_core.hpp", "common.hpp"),
+    "attn": ("attn.hip", "common.hpp"),
+    "lmhead": ("lmhead.hip", "gemm_core.hpp", "common.hpp"),
+    "rmsnorm": ("elementwise.hip", "common.hpp"),
+}
+
+
+def source_digest(kernel):
+    """sha256 over the sources of one timed kernel, in the order KERNEL_SOURCES lists them."""
     import hashlib
     h = hashlib.sha256()
-    root = os.path.dirname(os.path.abspath(__file__))
-    for p in sorted(glob.glob(os.path.join(root, "orthrus_round_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
+    root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "orthrus_round_amd", "csrc")
+    for name in KERNEL_SOURCES[kernel.split("_")[0]]:
+        with open(os.path.join(root, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
 def profiled_traffic(name):
     """HBM bytes per launch of a kernel from the committed FETCH_SIZE/WRITE_SIZE profile
-    (profiles/traffic.json, counts scaled by a plain 256 MiB copy), or None when the kernel
+    (profiles/traffic.json, counts scaled by a plain 256 MiB copy), or None when the kernel's
     sources changed after the counters were taken."""
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic.json")
     try:
@@ -158,10 +166,10 @@ def profiled_traffic(name):
             prof = json.load(f)
     except OSError:
         return None
-    if prof.get("source_sha256") != source_digest():
-        return None
     rec = prof.get("bench_kernels", {}).get(name)
-    return None if rec is None else rec["bytes"]
+    if rec is None or rec.get("source_sha256") != source_digest(name):
+        return None
+    return rec["bytes"]
 
 
 def roofline_of(name, rec, bound="hbm"):
