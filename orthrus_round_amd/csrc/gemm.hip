@@ -304,11 +304,15 @@ template <typename T> using KsBig = KsCfg<T, 64, 64, ORTHRUS_KSB_RINGS>;
 template <typename T> using PlainSmall = GemmCfg<T, 32, 128, 1, 4, 4, 4>;
 template <typename T> using PlainMid = GemmCfg<T, 64, 128, 2, 2, 3, 3>;
 template <typename T> using PlainBig = GemmCfg<T, 128, 128, 2, 2, ORTHRUS_PB_RINGS>;
-// 256-row tiles (a whole M = 256 round in one tile, so each weight tile is streamed once) run
-// eight wavefronts of 64x64: with one workgroup per CU that is still two wavefronts per SIMD.
-// The weight ring is the deeper one: it streams from HBM, the activation ring from L2.
+// Above 128 rows the wide family runs 128 x 192 tiles of eight 32 x 96 wavefronts (two per SIMD
+// at one workgroup per CU).  At M = 256 the 24576-wide gate/up projection is then 2 x 128 = 256
+// tiles, one per CU (256 x 128 tiles left 64 CUs idle), and each workgroup streams 2.5 MiB of
+// operands instead of 3; xcd_tile_map keeps the two row tiles of a weight tile on one XCD, so
+// the weights still come from HBM about once.  The weight ring is the deeper one: it streams
+// from HBM, the activation ring from L2.  (192 columns are three 64-column gate/up pairs, so the
+// SwiGLU epilogue never splits a pair.)
 #ifndef ORTHRUS_WIDE_HUGE_CFG
-#define ORTHRUS_WIDE_HUGE_CFG(T) GemmCfg<T, 256, 128, 4, 2, 2, 4>
+#define ORTHRUS_WIDE_HUGE_CFG(T) GemmCfg<T, 128, 192, 4, 2, 2, 4>
 #endif
 constexpr int kWideN = 16384;
 
