@@ -56,10 +56,11 @@ struct StageRings {
   static constexpr size_t RING_BYTES = (size_t)SA * A_STAGE + (size_t)SW * W_STAGE;
 };
 
-template <typename T, int BM_, int BN_, int WM_, int WN_, int SA_, int SW_>
+template <typename T, int BM_, int BN_, int WM_, int WN_, int SA_, int SW_, bool EVEN_ = false>
 struct GemmCfg : StageRings<T, BM_, BN_, SA_, SW_, WM_ * WN_> {
   static constexpr int WM = WM_, WN = WN_;
   static constexpr bool KSPLIT = false;
+  static constexpr bool EVEN_STAGES = EVEN_;
   static constexpr int TM = BM_ / (32 * WM), TN = BN_ / (32 * WN);
   static_assert(TM >= 1 && TN >= 1 && TM * 32 * WM == BM_ && TN * 32 * WN == BN_, "tile shape");
   static constexpr size_t TILE_BYTES = (size_t)BM_ * BN_ * 4;  // the fp32 tile parked for the epilogue
@@ -71,6 +72,7 @@ template <typename T, int BM_, int BN_, int SA_, int SW_>
 struct KsCfg : StageRings<T, BM_, BN_, SA_, SW_, 4> {
   static constexpr int WM = 1, WN = 1;
   static constexpr bool KSPLIT = true;
+  static constexpr bool EVEN_STAGES = false;
   static constexpr int TM = BM_ / 32, TN = BN_ / 32;
   static constexpr size_t PART_BYTES = (size_t)4 * TM * TN * 16 * 64 * 4;  // 4 waves' partial tiles
   static constexpr size_t RING = StageRings<T, BM_, BN_, SA_, SW_, 4>::RING_BYTES;
@@ -284,7 +286,9 @@ __device__ __forceinline__ void gemm_mainloop(const T* __restrict__ A, const T* 
       run_stage(kt, 0);
       run_stage(kt + 1, 1);
     }
-    if (kt < nk) {
+    if constexpr (Cfg::EVEN_STAGES) {
+      mma_part(fa[(2 * NP - 1) & 1], fb[(2 * NP - 1) & 1]);
+    } else if (kt < nk) {
       run_stage(kt, 0);
       mma_part(fa[(NP - 1) & 1], fb[(NP - 1) & 1]);
     } else {

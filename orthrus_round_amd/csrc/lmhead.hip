@@ -20,6 +20,7 @@ struct LmArgs {
   float* part_m;        // [rows, ntiles] max of z/T
   float* part_s;        // [rows, ntiles] sum exp(z/T - max)
   int32_t M, N, K, block, ntiles;
+  int32_t tile0;        // first 128-column tile of this launch
   float inv_t;          // 1/T (1 when greedy)
   int32_t sample;       // temperature > 0
   uint64_t seed, stream_id;
@@ -31,13 +32,17 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
   m = M;
 }
 
+constexpr int kLmBN = 128;
+
 template <typename T, typename Cfg>
 __global__ __launch_bounds__(Cfg::NT) ORTHRUS_GEMM_WAVES void lmhead_kernel(LmArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int mtiles = (a.M + Cfg::BM - 1) / Cfg::BM;
   int sp, mt, nt;
   xcd_tile_map(blockIdx.x, gridDim.x, 1, mtiles, sp, mt, nt);
-  const int m0 = mt * Cfg::BM, n0 = nt * Cfg::BN;
+  const int m0 = mt * Cfg::BM, n0 = a.tile0 * kLmBN + nt * Cfg::BN;
+  constexpr int P = Cfg::BN / kLmBN, WPP = Cfg::WN / P;  // partial tiles per workgroup, waves per partial
+  static_assert(P >= 1 && WPP >= 1 && P * kLmBN == Cfg::BN && WPP * P == Cfg::WN, "partials per 128 columns");
   f32x16 acc[Cfg::TM][Cfg::TN];
   gemm_mainloop<T, Cfg>(reinterpret_cast<const T*>(a.h), reinterpret_cast<const T*>(a.w), a.M, a.N, a.K, m0, n0, smem,
                         acc);
@@ -94,20 +99,23 @@ __global__ __launch_bounds__(Cfg::NT) ORTHRUS_GEMM_WAVES void lmhead_kernel(LmAr
     }
   }
   __syncthreads();
-  for (int mrow = threadIdx.x; mrow < Cfg::BM; mrow += Cfg::NT) {
+  for (int idx = threadIdx.x; idx < Cfg::BM * P; idx += Cfg::NT) {
+    const int mrow = idx / P, pt = idx % P;
     const int m = m0 + mrow;
-    if (m >= a.M) continue;
-    uint64_t best = red_best[mrow * Cfg::WN];
-    float lm = red_m[mrow * Cfg::WN], ls = red_s[mrow * Cfg::WN];
-    for (int q = 1; q < Cfg::WN; ++q) {
-      best = umax64(best, red_best[mrow * Cfg::WN + q]);
-      const float m2 = red_m[mrow * Cfg::WN + q];
+    const int tile = n0 / kLmBN + pt;
+    if (m >= a.M || tile >= a.ntiles) continue;
+    const int q0 = mrow * Cfg::WN + pt * WPP;
+    uint64_t best = red_best[q0];
+    float lm = red_m[q0], ls = red_s[q0];
+    for (int q = 1; q < WPP; ++q) {
+      best = umax64(best, red_best[q0 + q]);
+      const float m2 = red_m[q0 + q];
       if (m2 != -__builtin_huge_valf()) {
-        if (lm == -__builtin_huge_valf()) { lm = m2; ls = red_s[mrow * Cfg::WN + q]; }
-        else lse_merge(lm, ls, m2, red_s[mrow * Cfg::WN + q]);
+        if (lm == -__builtin_huge_valf()) { lm = m2; ls = red_s[q0 + q]; }
+        else lse_merge(lm, ls, m2, red_s[q0 + q]);
       }
     }
-    const size_t o = (size_t)m * a.ntiles + nt;
+    const size_t o = (size_t)m * a.ntiles + tile;
     a.part_best[o] = best;
     a.part_m[o] = lm;
     a.part_s[o] = ls;
@@ -162,15 +170,17 @@ __global__ __launch_bounds__(64) void lmhead_finalize(const uint64_t* part_best,
 }
 
 template <typename T, typename Cfg>
-int32_t launch(LmArgs& a, hipStream_t st) {
+int32_t launch(LmArgs& a, hipStream_t st, int tile0 = 0, int wg_tiles = -1) {
   const int mtiles = (a.M + Cfg::BM - 1) / Cfg::BM;
-  const size_t lds = std::max(Cfg::LDS_BYTES, (size_t)Cfg::BM * Cfg::WN * 16);
+  const size_t lds = std::max(Cfg::RING, (size_t)Cfg::BM * Cfg::WN * 16);
+  if (wg_tiles < 0) wg_tiles = (a.ntiles - tile0) / (Cfg::BN / kLmBN) + ((a.ntiles - tile0) % (Cfg::BN / kLmBN) != 0);
+  if (wg_tiles == 0) return ORTHRUS_OK;
+  a.tile0 = tile0;
   allow_lds(lmhead_kernel<T, Cfg>, lds);
-  hipLaunchKernelGGL((lmhead_kernel<T, Cfg>), dim3(mtiles * a.ntiles), dim3(Cfg::NT), lds, st, a);
+  hipLaunchKernelGGL((lmhead_kernel<T, Cfg>), dim3(mtiles * wg_tiles), dim3(Cfg::NT), lds, st, a);
   return check_launch("orthrus_lmhead_argmax");
 }
 
-constexpr int kLmBN = 128;
 #ifndef ORTHRUS_LM_BIG_CFG
 #define ORTHRUS_LM_BIG_CFG(T) GemmCfg<T, 128, kLmBN, 2, 2, 3, 2>
 #endif
@@ -178,6 +188,30 @@ constexpr int kLmBN = 128;
 #ifndef ORTHRUS_LM_HUGE_CFG
 #define ORTHRUS_LM_HUGE_CFG(T) GemmCfg<T, 256, kLmBN, 4, 2, 2, 4>
 #endif
+// 256x256 pair tiles: eight 64x128 wavefronts, rings of two stages (128 KiB), main loop without the
+// odd-stage tail (the host only takes this path when the stage count is even)
+template <typename T> using LmPairCfg = GemmCfg<T, 256, 256, 4, 2, 2, 2, true>;
+
+// Above 128 rows with an even number of k-stages: whole waves of 256x256 workgroups (eight 64x128
+// wavefronts, each owning one 128-column partial tile), then the remaining tiles as 256x128
+// workgroups in a second launch.  A 256x256 workgroup re-reads the 2 MiB activation tile from L2
+// once per 256 columns instead of once per 128, which is what bounds the LM head; a grid of only
+// 256x256 tiles would leave a last wave of 82 workgroups on 256 CUs at V = 151936, hence the mix.
+// The partials stay per 128-column tile, so the finalize merge is the same whatever the split.
+template <typename T>
+int32_t launch_mixed(LmArgs& a, hipStream_t st) {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  }
+  const int mtiles = (a.M + 255) / 256;
+  const int rounds = (a.ntiles * mtiles) / (2 * cus);
+  int npairs = std::min(a.ntiles / 2, rounds * cus / mtiles);
+  if (int32_t s = launch<T, LmPairCfg<T>>(a, st, 0, npairs)) return s;
+  return launch<T, ORTHRUS_LM_HUGE_CFG(T)>(a, st, 2 * npairs);
+}
 
 }  // namespace
 }  // namespace orthrus
@@ -207,6 +241,7 @@ extern "C" int32_t orthrus_lmhead_argmax(const orthrus_lmhead_desc_t* d, const v
   ORTHRUS_REQUIRE(ws && ws_bytes >= need, ORTHRUS_ERR_WORKSPACE, "lmhead: workspace %zu < %zu", ws_bytes, need);
   if (d->rows == 0) return ORTHRUS_OK;
   LmArgs a;
+  a.tile0 = 0;
   a.h = h; a.w = w; a.seq_id = seq_id; a.round = round; a.logits = logits_out;
   a.M = d->rows; a.N = d->vocab; a.K = d->hidden; a.block = d->block > 0 ? d->block : 1;
   a.ntiles = (d->vocab + kLmBN - 1) / kLmBN;
@@ -223,6 +258,7 @@ extern "C" int32_t orthrus_lmhead_argmax(const orthrus_lmhead_desc_t* d, const v
     if (a.M <= 32) s = launch<bf16, GemmCfg<bf16, 32, kLmBN, 1, 4, 4, 4>>(a, st);
     else if (a.M <= 64) s = launch<bf16, GemmCfg<bf16, 64, kLmBN, 2, 2, 3, 3>>(a, st);
     else if (a.M <= 128) s = launch<bf16, ORTHRUS_LM_BIG_CFG(bf16)>(a, st);
+    else if (a.K % 128 == 0) s = launch_mixed<bf16>(a, st);
     else s = launch<bf16, ORTHRUS_LM_HUGE_CFG(bf16)>(a, st);
   } else {
     if (a.M <= 32) s = launch<float, GemmCfg<float, 32, kLmBN, 1, 4, 4, 4>>(a, st);
