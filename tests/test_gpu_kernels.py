@@ -56,8 +56,13 @@ def lmhead(h, w, dtype, temperature=0.0, seed=0, block=32, seq=None, rnd=None, w
 
 # ------------------------------------------------------------------- LM head
 
+# Above 128 rows: 511*128 + 77 columns are 512 tiles, two whole waves of 256x256 pair workgroups whose
+# last pair holds the ragged tile; 515 tiles at 300 rows leave a 256x128 rest of three tiles per row
+# tile; hidden 192 (an odd number of k-stages) takes the 256x128 layout alone.
 @pytest.mark.parametrize("rows,hidden,vocab,dtype", [(64, 256, 4096, ora.F32), (37, 256, 4000, ora.BF16),
-                                                     (128, 512, 1024 + 64, ora.BF16), (8, 4096, 8192, ora.BF16)])
+                                                     (128, 512, 1024 + 64, ora.BF16), (8, 4096, 8192, ora.BF16),
+                                                     (256, 256, 511 * 128 + 77, ora.BF16),
+                                                     (300, 256, 515 * 128, ora.BF16), (256, 192, 70000, ora.BF16)])
 def test_lmhead_argmax_small(rows, hidden, vocab, dtype):
     h, w = synth.lmhead_inputs(8, rows, hidden, vocab, bf16=(dtype == ora.BF16))
     tok, lse, logits = lmhead(h, w, dtype, block=1, want_logits=True)
@@ -437,9 +442,14 @@ def test_zero_sized_calls_launch_nothing():
     st = [i32() for _ in range(7)]
     outs = torch.full((1, 8), 7, dtype=torch.int32, device=DEV)
     ora.consensus_commit(0, 32, st[0], st[1], st[2], st[3], st[4], outs, st[5], st[6], i32(), 8, 64)
+    lse = torch.zeros(4, dtype=torch.float32, device=DEV)
+    fill = [i32() for _ in range(3)]
+    ora.draft_fill(0, 32, 256, 512, ora.BF16, a, w, lse, i32(), 511, 15, fill[0], fill[1])
+    ora.draft_merge(0, 32, i32(), i32(), i32(), fill[2])
     torch.cuda.synchronize()
     assert bool((c == 3.0).all()) and bool((y == 3.0).all()) and bool((tok == 7).all())
     assert bool((out == 5.0).all()) and bool((outs == 7).all()) and all(bool((t == 7).all()) for t in st)
+    assert all(bool((t == 7).all()) for t in fill)
 
 
 @pytest.mark.parametrize("dtype", [ora.BF16, ora.F32])
