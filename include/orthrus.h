@@ -190,13 +190,14 @@ typedef enum {
 /* c [M, N'] = epilogue(a [M, K] . w [N, K]^T), fp32 accumulation.  K % 64 == 0; SwiGLU needs
  * N % 64 == 0.  The summation order of an output element depends on (N, K) only, so a row
  * computed alone has the same bits as the same row inside a larger batch:
- *  - N < 16384 with K a multiple of 256 (bf16) or 128 (fp32): K is cut into four contiguous
- *    quarters, each summed in k order into an fp32 partial, and the four partials are added in
- *    quarter order before the epilogue;
+ *  - N < 16384 with K a multiple of 256 (bf16) or 128 (fp32): K is cut into S contiguous slices
+ *    (S = 8 when K >= 8192 and K is a multiple of 512 (bf16) or 256 (fp32), else S = 4), each
+ *    summed in k order into an fp32 partial, and the S partials are added in slice order before
+ *    the epilogue;
  *  - other N < 16384: the k-steps of a tile are dealt four ways inside one workgroup and the
  *    four partial sums are added in a fixed order;
  *  - N >= 16384: one k loop in order.
- * Workspace: orthrus_gemm_workspace_bytes() bytes (4 * M * N * 4 for the quarter split, else 0),
+ * Workspace: orthrus_gemm_workspace_bytes() bytes (S * M * N * 4 for the k-split, else 0),
  * 16-byte aligned, caller-owned, contents undefined on entry and exit; a smaller workspace
  * returns ORTHRUS_ERR_WORKSPACE before anything is launched.  Calls that overlap on one
  * workspace race. */
@@ -210,8 +211,8 @@ int32_t orthrus_gemm(int32_t M, int32_t N, int32_t K, int32_t dtype, int32_t out
  *   x [M, N] = x + a [M, K] . w [N, K]^T   (in place, the residual stream, `dtype`)
  *   y [M, N] = x / sqrt(mean(x^2) + eps) * gain   (gain fp32 [N]; y in `dtype`)
  * The result has exactly the bits of orthrus_gemm(..., ORTHRUS_EPI_RESIDUAL, residual = c = x) followed
- * by orthrus_rmsnorm(M, N, dtype, x, gain, eps, y).  Where the GEMM takes the k-quarter split and a
- * row is at most 1024 16-byte chunks (x, y 16-byte aligned), the quarter partials are added, the
+ * by orthrus_rmsnorm(M, N, dtype, x, gain, eps, y).  Where the GEMM takes the k-split and a
+ * row is at most 1024 16-byte chunks (x, y 16-byte aligned), the slice partials are added, the
  * residual updated and the row normalised in one pass; otherwise the two calls run in sequence.
  * Workspace as orthrus_gemm with ORTHRUS_EPI_RESIDUAL; y must not overlap x. */
 int32_t orthrus_gemm_residual_rmsnorm(int32_t M, int32_t N, int32_t K, int32_t dtype, const void* a,
@@ -234,7 +235,7 @@ int32_t orthrus_rope_table(int32_t max_pos, int32_t head_dim, double base, float
 /* The QKV projection and the RoPE + K/V write that follows it in the layer body, in one call:
  * qkv = a [batch*block, hidden] . w [(Hq + 2 Hkv) * D, hidden]^T, then orthrus_rope_kv_write on it.
  * The result has exactly the bits of orthrus_gemm(..., ORTHRUS_EPI_STORE, c = qkv) followed by
- * orthrus_rope_kv_write(..., qkv, ...).  Where the GEMM takes the k-quarter split, the partials are
+ * orthrus_rope_kv_write(..., qkv, ...).  Where the GEMM takes the k-split, the partials are
  * added, rotated and written row by row and `qkv` is not touched; otherwise the two calls run in
  * sequence through `qkv` (caller-owned [batch*block, (Hq + 2 Hkv) * D], contents undefined after).
  * Workspace as orthrus_gemm with ORTHRUS_EPI_STORE. */

@@ -1,9 +1,9 @@
 // Layer GEMMs of both views: C = epilogue(A W^T) on MFMA with fused residual add or SwiGLU.
 //
-// Narrow outputs (N < 16384: the q/k/v, O and down projections) split K into four contiguous
-// quarters, one workgroup per (tile, quarter): each runs the plain MFMA chain over its quarter and
-// writes an fp32 partial tile, and a second kernel adds the four partials in quarter order and
-// applies the epilogue.  Splitting K across workgroups keeps 256+ workgroups busy with 128x128
+// Narrow outputs (N < 16384: the q/k/v, O and down projections) split K into S contiguous slices
+// (S = 4, or 8 for the deep down projection), one workgroup per (tile, slice): each runs the plain
+// MFMA chain over its slice and writes an fp32 partial tile, and a second kernel adds the S
+// partials in slice order and applies the epilogue.  Splitting K across workgroups keeps 256+ workgroups busy with 128x128
 // tiles, which stream half the operand bytes of 64x64 tiles through L2.  Wide outputs (gate/up)
 // use plain tiles over the whole K.  Either way an output element's summation order depends on
 // (N, K) only, so results are deterministic and a row's bits do not depend on the batch size.
@@ -74,19 +74,19 @@ __global__ __launch_bounds__(Cfg::NT) ORTHRUS_GEMM_WAVES void gemm_kernel(const 
   }
 }
 
-// One k-quarter of a BM x BN tile: the plain MFMA chain over k in [q K/4, (q+1) K/4), stored as an
+// One k-slice of a BM x BN tile: the plain MFMA chain over k in [q K/S, (q+1) K/S), stored as an
 // fp32 partial tile in P[q][M][N] straight from the accumulators (32 lanes write 32 consecutive
 // columns of one row).
 template <typename T, typename Cfg>
 __global__ __launch_bounds__(Cfg::NT) ORTHRUS_GEMM_WAVES void gemm_quarter_kernel(const T* __restrict__ A,
                                                                                 const T* __restrict__ W,
                                                                                 float* __restrict__ P, int M, int N,
-                                                                                int K) {
+                                                                                int K, int S) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int mtiles = (M + Cfg::BM - 1) / Cfg::BM;
   int q, mt, nt;
-  xcd_tile_map(blockIdx.x, gridDim.x, 4, mtiles, q, mt, nt);
-  const int m0 = mt * Cfg::BM, n0 = nt * Cfg::BN, kq = K / 4;
+  xcd_tile_map(blockIdx.x, gridDim.x, S, mtiles, q, mt, nt);
+  const int m0 = mt * Cfg::BM, n0 = nt * Cfg::BN, kq = K / S;
   f32x16 acc[Cfg::TM][Cfg::TN];
   gemm_mainloop<T, Cfg>(A + (size_t)q * kq, W + (size_t)q * kq, M, N, K, m0, n0, smem, acc, kq);
   const int lane = threadIdx.x & 63, hh = lane >> 5, r = lane & 31;
@@ -107,10 +107,10 @@ __global__ __launch_bounds__(Cfg::NT) ORTHRUS_GEMM_WAVES void gemm_quarter_kerne
     }
 }
 
-// c = epilogue(P0 + P1 + P2 + P3), the partials added in quarter order.  V consecutive output
+// c = epilogue(((P0 + P1) + P2) + ...), the S partials added in slice order.  V consecutive output
 // columns per thread (V = 4 when the row length allows 16-byte partial loads).  SwiGLU columns come
 // in (gate 32, up 32) groups, as in the plain epilogue.
-template <typename OutT, int EPI, int V>
+template <typename OutT, int EPI, int V, int S>
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restrict__ P, const OutT* residual, OutT* C,
                                                          int M, int N) {
   const size_t MN = (size_t)M * N;
@@ -121,13 +121,22 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restric
   auto sum = [&](int n, float (&s)[V]) {
     const size_t o = (size_t)m * N + n;
     if constexpr (V == 4) {
-      const f32x4 p0 = *reinterpret_cast<const f32x4*>(P + o), p1 = *reinterpret_cast<const f32x4*>(P + o + MN);
-      const f32x4 p2 = *reinterpret_cast<const f32x4*>(P + o + 2 * MN);
-      const f32x4 p3 = *reinterpret_cast<const f32x4*>(P + o + 3 * MN);
+      f32x4 pp[S];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) s[v] = ((p0[v] + p1[v]) + p2[v]) + p3[v];
+      for (int q = 0; q < S; ++q) pp[q] = *reinterpret_cast<const f32x4*>(P + o + q * MN);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        s[v] = pp[0][v];
+#pragma unroll
+        for (int q = 1; q < S; ++q) s[v] += pp[q][v];
+      }
     } else {
-      s[0] = ((P[o] + P[o + MN]) + P[o + 2 * MN]) + P[o + 3 * MN];
+      float pp[S];
+#pragma unroll
+      for (int q = 0; q < S; ++q) pp[q] = P[o + q * MN];
+      s[0] = pp[0];
+#pragma unroll
+      for (int q = 1; q < S; ++q) s[0] += pp[q];
     }
   };
   float x[V];
@@ -149,13 +158,13 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restric
   for (int v = 0; v < V; ++v) C[idx + v] = from_f32<OutT>(x[v]);
 }
 
-// The residual k-quarter reduce fused with the RMSNorm that follows every residual GEMM of a layer:
-// x = x + (P0 + P1 + P2 + P3) (stored), then y = rmsnorm(x) * g.  One workgroup per row.  Each thread
+// The residual k-slice reduce fused with the RMSNorm that follows every residual GEMM of a layer:
+// x = x + (((P0 + P1) + P2) + ...) (stored), then y = rmsnorm(x) * g.  One workgroup per row.  Each thread
 // owns the same 16-byte chunks of the row as rmsnorm_kernel (chunk c = q * 256 + tid) and the sum of
 // squares runs over the stored (rounded) x in the same order (per thread in chunk order, a wave
 // butterfly, then the four waves in order), so the result has the bits of the residual GEMM
 // followed by orthrus_rmsnorm.
-template <typename T>
+template <typename T, int S>
 __global__ __launch_bounds__(256) void gemm_reduce_rmsnorm_kernel(const float* __restrict__ P, T* x,
                                                                   const float* __restrict__ g, float eps, int M,
                                                                   int N, T* __restrict__ y) {
@@ -179,11 +188,16 @@ __global__ __launch_bounds__(256) void gemm_reduce_rmsnorm_kernel(const float* _
 #pragma unroll
       for (int i = 0; i < EPC; i += 4) {
         const size_t o = (size_t)c * EPC + i;
-        const f32x4 p0 = *reinterpret_cast<const f32x4*>(pr + o), p1 = *reinterpret_cast<const f32x4*>(pr + o + MN);
-        const f32x4 p2 = *reinterpret_cast<const f32x4*>(pr + o + 2 * MN);
-        const f32x4 p3 = *reinterpret_cast<const f32x4*>(pr + o + 3 * MN);
+        f32x4 pp[S];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) xe[i + v] = from_f32<T>(to_f32(re[i + v]) + (((p0[v] + p1[v]) + p2[v]) + p3[v]));
+        for (int k = 0; k < S; ++k) pp[k] = *reinterpret_cast<const f32x4*>(pr + o + k * MN);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float sum = pp[0][v];
+#pragma unroll
+          for (int k = 1; k < S; ++k) sum += pp[k][v];
+          xe[i + v] = from_f32<T>(to_f32(re[i + v]) + sum);
+        }
       }
       *reinterpret_cast<u32x4_t*>(xr + (size_t)c * EPC) = buf[q];
     }
@@ -220,13 +234,13 @@ __global__ __launch_bounds__(256) void gemm_reduce_rmsnorm_kernel(const float* _
   }
 }
 
-// The q/k/v k-quarter reduce fused with RoPE and the K/V write (rope_kv_kernel's work): every q/k/v
-// element is the sum of the four partials in quarter order rounded to T, exactly the value the store
+// The q/k/v k-slice reduce fused with RoPE and the K/V write (rope_kv_kernel's work): every q/k/v
+// element is the sum of the S partials in slice order rounded to T, exactly the value the store
 // epilogue would have written, and the rotation and the writes are rope_kv_kernel's, so the result has
 // the bits of orthrus_gemm(STORE) followed by orthrus_rope_kv_write.  Workgroup (row m, head group y)
 // handles 256 / (D/2) consecutive heads of the row's Hq + Hkv rotated heads and Hkv value heads, one
 // rotation pair (or two copied value elements) per thread.
-template <typename T>
+template <typename T, int S>
 __global__ __launch_bounds__(256) void gemm_reduce_rope_kv_kernel(const float* __restrict__ P, int M,
                                                                   const float* __restrict__ table, int max_pos,
                                                                   const int32_t* __restrict__ ctx_len,
@@ -243,7 +257,10 @@ __global__ __launch_bounds__(256) void gemm_reduce_rope_kv_kernel(const float* _
   const size_t MN = (size_t)M * width;
   const float* pr = P + (size_t)m * width;
   auto val = [&](int j) {
-    return to_f32(from_f32<T>(((pr[j] + pr[j + MN]) + pr[j + 2 * MN]) + pr[j + 3 * MN]));
+    float sum = pr[j];
+#pragma unroll
+    for (int k = 1; k < S; ++k) sum += pr[j + k * MN];
+    return to_f32(from_f32<T>(sum));
   };
   const bool pos_ok = pos >= 0 && pos < max_pos;
   size_t kv_base = 0;
@@ -345,60 +362,77 @@ int32_t launch_cfg(int M, int N, int K, int epi, const void* a, const void* w, c
   return check_launch("orthrus_gemm");
 }
 
-// The quarter split needs each quarter of K to be whole 128-byte stages.
-bool quarter_split(int N, int K, int dtype) {
+// The k-split: S contiguous slices of K, each a whole number of 128-byte stages.  S = 8 for deep K
+// (the down projection: 128x128 tiles x 8 slices put two workgroups on every CU, 49-50 us against
+// 58-64 at M = 256), 4 otherwise (8 slices made q/k/v and O slower); 0 when K does not split or N
+// is wide.  A function of (N, K) only, so a row's summation order never depends on M.
+int k_splits(int N, int K, int dtype) {
   const int bk = dtype == ORTHRUS_BF16 ? 64 : 32;
-  return N < kWideN && K % (4 * bk) == 0;
+  if (N >= kWideN) return 0;
+  if (K >= 8192 && K % (8 * bk) == 0) return 8;
+  return K % (4 * bk) == 0 ? 4 : 0;
 }
 
-// The four k-quarter partial tiles of a [M, N] product into P; the tile height follows M only.
+template <typename T> constexpr int dtype_of() { return sizeof(T) == 2 ? ORTHRUS_BF16 : ORTHRUS_F32; }
+
+// The S k-slice partial tiles of a [M, N] product into P; the tile height follows M only.
 template <typename T, typename Cfg>
-void launch_quarter_cfg(int M, int N, int K, const void* a, const void* w, float* P, hipStream_t st) {
+void launch_quarter_cfg(int M, int N, int K, int S, const void* a, const void* w, float* P, hipStream_t st) {
   const int mtiles = (M + Cfg::BM - 1) / Cfg::BM, ntiles = (N + Cfg::BN - 1) / Cfg::BN;
   allow_lds(gemm_quarter_kernel<T, Cfg>, Cfg::RING);
-  hipLaunchKernelGGL((gemm_quarter_kernel<T, Cfg>), dim3(4 * mtiles * ntiles), dim3(Cfg::NT), Cfg::RING, st,
-                     reinterpret_cast<const T*>(a), reinterpret_cast<const T*>(w), P, M, N, K);
+  hipLaunchKernelGGL((gemm_quarter_kernel<T, Cfg>), dim3(S * mtiles * ntiles), dim3(Cfg::NT), Cfg::RING, st,
+                     reinterpret_cast<const T*>(a), reinterpret_cast<const T*>(w), P, M, N, K, S);
 }
 
+// Returns S, the number of partial tiles written.
 template <typename T>
-void launch_quarter_tiles(int M, int N, int K, const void* a, const void* w, float* P, hipStream_t st) {
-  if (M <= 32) launch_quarter_cfg<T, PlainSmall<T>>(M, N, K, a, w, P, st);
-  else if (M <= 64) launch_quarter_cfg<T, PlainMid<T>>(M, N, K, a, w, P, st);
-  else launch_quarter_cfg<T, PlainBig<T>>(M, N, K, a, w, P, st);
+int launch_quarter_tiles(int M, int N, int K, const void* a, const void* w, float* P, hipStream_t st) {
+  const int S = k_splits(N, K, dtype_of<T>());
+  if (M <= 32) launch_quarter_cfg<T, PlainSmall<T>>(M, N, K, S, a, w, P, st);
+  else if (M <= 64) launch_quarter_cfg<T, PlainMid<T>>(M, N, K, S, a, w, P, st);
+  else launch_quarter_cfg<T, PlainBig<T>>(M, N, K, S, a, w, P, st);
+  return S;
 }
 
-template <typename T, typename OutT>
-int32_t launch_quarters(int M, int N, int K, int epi, const void* a, const void* w, const void* res, void* c,
-                        float* P, hipStream_t st) {
-  launch_quarter_tiles<T>(M, N, K, a, w, P, st);
-  const OutT* R = reinterpret_cast<const OutT*>(res);
-  OutT* C = reinterpret_cast<OutT*>(c);
+template <typename OutT, int S>
+void launch_reduce(int M, int N, int epi, const float* P, const OutT* R, OutT* C, hipStream_t st) {
   const size_t outs = (size_t)M * (epi == ORTHRUS_EPI_SWIGLU ? N / 2 : N);
   // 16-byte partial loads need every row to start on a 4-column boundary (SwiGLU: N % 64 == 0)
   if (N % 4 == 0) {
     const dim3 rgrid((unsigned)((outs / 4 + 255) / 256));
     if (epi == ORTHRUS_EPI_STORE)
-      hipLaunchKernelGGL((gemm_reduce_kernel<OutT, ORTHRUS_EPI_STORE, 4>), rgrid, dim3(256), 0, st, P, R, C, M, N);
+      hipLaunchKernelGGL((gemm_reduce_kernel<OutT, ORTHRUS_EPI_STORE, 4, S>), rgrid, dim3(256), 0, st, P, R, C, M, N);
     else if (epi == ORTHRUS_EPI_RESIDUAL)
-      hipLaunchKernelGGL((gemm_reduce_kernel<OutT, ORTHRUS_EPI_RESIDUAL, 4>), rgrid, dim3(256), 0, st, P, R, C, M, N);
+      hipLaunchKernelGGL((gemm_reduce_kernel<OutT, ORTHRUS_EPI_RESIDUAL, 4, S>), rgrid, dim3(256), 0, st, P, R, C, M,
+                         N);
     else
-      hipLaunchKernelGGL((gemm_reduce_kernel<OutT, ORTHRUS_EPI_SWIGLU, 4>), rgrid, dim3(256), 0, st, P, R, C, M, N);
+      hipLaunchKernelGGL((gemm_reduce_kernel<OutT, ORTHRUS_EPI_SWIGLU, 4, S>), rgrid, dim3(256), 0, st, P, R, C, M, N);
   } else {
     const dim3 rgrid((unsigned)((outs + 255) / 256));
     if (epi == ORTHRUS_EPI_STORE)
-      hipLaunchKernelGGL((gemm_reduce_kernel<OutT, ORTHRUS_EPI_STORE, 1>), rgrid, dim3(256), 0, st, P, R, C, M, N);
+      hipLaunchKernelGGL((gemm_reduce_kernel<OutT, ORTHRUS_EPI_STORE, 1, S>), rgrid, dim3(256), 0, st, P, R, C, M, N);
     else
-      hipLaunchKernelGGL((gemm_reduce_kernel<OutT, ORTHRUS_EPI_RESIDUAL, 1>), rgrid, dim3(256), 0, st, P, R, C, M, N);
+      hipLaunchKernelGGL((gemm_reduce_kernel<OutT, ORTHRUS_EPI_RESIDUAL, 1, S>), rgrid, dim3(256), 0, st, P, R, C, M,
+                         N);
   }
+}
+
+template <typename T, typename OutT>
+int32_t launch_quarters(int M, int N, int K, int epi, const void* a, const void* w, const void* res, void* c,
+                        float* P, hipStream_t st) {
+  const int S = launch_quarter_tiles<T>(M, N, K, a, w, P, st);
+  const OutT* R = reinterpret_cast<const OutT*>(res);
+  OutT* C = reinterpret_cast<OutT*>(c);
+  if (S == 8) launch_reduce<OutT, 8>(M, N, epi, P, R, C, st);
+  else launch_reduce<OutT, 4>(M, N, epi, P, R, C, st);
   return check_launch("orthrus_gemm");
 }
 
 template <typename T, typename OutT>
 int32_t launch(int M, int N, int K, int epi, const void* a, const void* w, const void* res, void* c, float* P,
                hipStream_t st) {
-  constexpr int BK = 8 * (16 / (int)sizeof(T));  // k per 128-byte stage
   if (N < kWideN) {
-    if (K % (4 * BK) == 0) return launch_quarters<T, OutT>(M, N, K, epi, a, w, res, c, P, st);
+    if (k_splits(N, K, dtype_of<T>())) return launch_quarters<T, OutT>(M, N, K, epi, a, w, res, c, P, st);
     if (M <= 32) return launch_cfg<T, OutT, KsSmall<T>>(M, N, K, epi, a, w, res, c, st);
     return launch_cfg<T, OutT, KsBig<T>>(M, N, K, epi, a, w, res, c, st);
   }
@@ -408,21 +442,25 @@ int32_t launch(int M, int N, int K, int epi, const void* a, const void* w, const
   return launch_cfg<T, OutT, ORTHRUS_WIDE_HUGE_CFG(T)>(M, N, K, epi, a, w, res, c, st);
 }
 
-// The fused residual + RMSNorm pass applies when the GEMM takes the quarter split and the row fits
+// The fused residual + RMSNorm pass applies when the GEMM takes the k-split and the row fits
 // rmsnorm_kernel's register path (16-byte chunks, at most 1024 of them, 16-byte aligned rows).
 template <typename T>
 bool fused_norm_ok(int N, int K, int dtype, const void* x, const void* y) {
   constexpr int EPC = 16 / (int)sizeof(T);
-  return quarter_split(N, K, dtype) && N % EPC == 0 && N / EPC <= 4 * 256 &&
+  return k_splits(N, K, dtype) && N % EPC == 0 && N / EPC <= 4 * 256 &&
          ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15) == 0;
 }
 
 template <typename T>
 int32_t launch_residual_rmsnorm(int M, int N, int K, const void* a, const void* w, void* x, const float* gain,
                                 float eps, void* y, float* P, hipStream_t st) {
-  launch_quarter_tiles<T>(M, N, K, a, w, P, st);
-  hipLaunchKernelGGL(gemm_reduce_rmsnorm_kernel<T>, dim3(M), dim3(256), 0, st, P, reinterpret_cast<T*>(x), gain, eps,
-                     M, N, reinterpret_cast<T*>(y));
+  const int S = launch_quarter_tiles<T>(M, N, K, a, w, P, st);
+  if (S == 8)
+    hipLaunchKernelGGL((gemm_reduce_rmsnorm_kernel<T, 8>), dim3(M), dim3(256), 0, st, P, reinterpret_cast<T*>(x), gain,
+                       eps, M, N, reinterpret_cast<T*>(y));
+  else
+    hipLaunchKernelGGL((gemm_reduce_rmsnorm_kernel<T, 4>), dim3(M), dim3(256), 0, st, P, reinterpret_cast<T*>(x), gain,
+                       eps, M, N, reinterpret_cast<T*>(y));
   return check_launch("orthrus_gemm_residual_rmsnorm");
 }
 
@@ -454,8 +492,8 @@ using namespace orthrus;
 
 extern "C" size_t orthrus_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t dtype, int32_t epilogue) {
   (void)epilogue;
-  if (M <= 0 || N <= 0 || K <= 0 || !quarter_split(N, K, dtype)) return 0;
-  return (size_t)4 * M * N * sizeof(float);  // the four fp32 k-quarter partials
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return (size_t)k_splits(N, K, dtype) * M * N * sizeof(float);  // the S fp32 k-slice partials
 }
 
 extern "C" int32_t orthrus_gemm(int32_t M, int32_t N, int32_t K, int32_t dtype, int32_t out_dtype, int32_t epilogue,
@@ -524,7 +562,7 @@ extern "C" int32_t orthrus_gemm_rope_kv_write(int32_t batch, int32_t block, int3
   ORTHRUS_REQUIRE(need == 0 || ((uintptr_t)workspace & 15) == 0, ORTHRUS_ERR_INVALID_ARG,
                   "gemm_rope_kv_write: workspace not 16-byte aligned");
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (!quarter_split(N, K, dtype) || head_dim > 512 || 256 % (head_dim / 2) != 0) {
+  if (!k_splits(N, K, dtype) || head_dim > 512 || 256 % (head_dim / 2) != 0) {
     // other shapes: the two calls in sequence through qkv (the fused pass has their bits)
     if (int32_t s = orthrus_gemm(M, N, K, dtype, dtype, ORTHRUS_EPI_STORE, a, w, nullptr, qkv, workspace,
                                  workspace_bytes, stream))
@@ -535,12 +573,17 @@ extern "C" int32_t orthrus_gemm_rope_kv_write(int32_t batch, int32_t block, int3
   float* P = reinterpret_cast<float*>(workspace);
   auto quarters = [&](auto tag) {
     using T = decltype(tag);
-    launch_quarter_tiles<T>(M, N, K, a, w, P, st);
+    const int S = launch_quarter_tiles<T>(M, N, K, a, w, P, st);
     const int hpw = 256 / (head_dim / 2);
-    hipLaunchKernelGGL(gemm_reduce_rope_kv_kernel<T>, dim3(M, (q_heads + 2 * kv_heads + hpw - 1) / hpw), dim3(256), 0,
-                       st, P, M, rope_table, max_pos, ctx_len,
-                       page_table, block, q_heads, kv_heads, head_dim, page_size, max_pages, reinterpret_cast<T*>(q_out),
-                       reinterpret_cast<T*>(k_dst), reinterpret_cast<T*>(v_dst));
+    const dim3 grid(M, (q_heads + 2 * kv_heads + hpw - 1) / hpw);
+    if (S == 8)
+      hipLaunchKernelGGL((gemm_reduce_rope_kv_kernel<T, 8>), grid, dim3(256), 0, st, P, M, rope_table, max_pos, ctx_len,
+                         page_table, block, q_heads, kv_heads, head_dim, page_size, max_pages,
+                         reinterpret_cast<T*>(q_out), reinterpret_cast<T*>(k_dst), reinterpret_cast<T*>(v_dst));
+    else
+      hipLaunchKernelGGL((gemm_reduce_rope_kv_kernel<T, 4>), grid, dim3(256), 0, st, P, M, rope_table, max_pos, ctx_len,
+                         page_table, block, q_heads, kv_heads, head_dim, page_size, max_pages,
+                         reinterpret_cast<T*>(q_out), reinterpret_cast<T*>(k_dst), reinterpret_cast<T*>(v_dst));
   };
   if (dtype == ORTHRUS_BF16) quarters(bf16{});
   else quarters(float{});

@@ -119,7 +119,7 @@ class Decoder:
         for (n, k, e) in ((self.nqkv, H, L.EPI_STORE), (H, Hq * D, L.EPI_RESIDUAL), (2 * I, H, L.EPI_SWIGLU),
                           (H, I, L.EPI_RESIDUAL)):
             gw = max(gw, L.gemm_workspace_bytes(M, n, k, self.dt, e))
-        self.gemm_ws = torch.empty(max(gw, 256), dtype=torch.uint8, device=self.dev)  # k-quarter partials
+        self.gemm_ws = torch.empty(max(gw, 256), dtype=torch.uint8, device=self.dev)  # k-split partials
         self.lm_ws = torch.empty(L.lmhead_workspace_bytes(L.lmhead_desc(M, H, V, self.dt)), dtype=torch.uint8,
                                  device=self.dev)
         # round state

@@ -91,6 +91,9 @@ def test_gemm_workspace_holds_the_k_quarter_partials():
     assert ora.gemm_workspace_bytes(256, 4096, 4096, ora.BF16, ora.EPI_STORE) == 4 * 256 * 4096 * 4
     assert ora.gemm_workspace_bytes(8, 6144, 4096, ora.F32, ora.EPI_RESIDUAL) == 4 * 8 * 6144 * 4
     assert ora.gemm_workspace_bytes(8, 6144, 128, ora.F32, ora.EPI_STORE) == 4 * 8 * 6144 * 4
+    # deep K (the down projection) splits eight ways
+    assert ora.gemm_workspace_bytes(256, 4096, 12288, ora.BF16, ora.EPI_RESIDUAL) == 8 * 256 * 4096 * 4
+    assert ora.gemm_workspace_bytes(8, 4096, 8192 + 256, ora.BF16, ora.EPI_RESIDUAL) == 4 * 8 * 4096 * 4
     # the wide (gate/up) family and K that does not split into whole 128-byte stages need none
     assert ora.gemm_workspace_bytes(8, 24576, 4096, ora.BF16, ora.EPI_SWIGLU) == 0
     assert ora.gemm_workspace_bytes(8, 4096, 192, ora.BF16, ora.EPI_STORE) == 0
