@@ -17,7 +17,13 @@ Parity status per function (pins live in ``tests/test_oracle_*.py``):
 * draft_pass ................... pinned to the same Llama with a block mask when both views share weights
 * argmax ....................... ties -> lowest id, pinned by duplicated LM-head rows
 * consensus .................... exhaustive first-mismatch closed form
-* rejection_accept / race ...... exact acceptance probability and chi-square on a tiny vocabulary
+* softmax_t ..................... scipy / torch softmax of z/T in float64, two-logit closed form
+* gumbel_sample ................. chi-square against scipy's softmax(z/T) on seeded Philox draws,
+                                 greedy in the T -> 0 limit
+* rejection_accept / race ...... acceptance rate sum(min(p, q)) and output law p (p, q from scipy),
+                                 greedy consensus in the T -> 0 limit
+* generate / generate_ar, T > 0  first two committed tokens follow the AR law p(t1) p(t2 | t1)
+                                 (chi-square over seeded runs on a one-layer, 8-token decoder)
 * generate vs generate_ar ...... losslessness (identical greedy trajectories), forced full/zero
                                  acceptance, K = 1, poisoned dead cache slots
 * token values on random weights: parity unpinned by the pages (no worked example exists);
