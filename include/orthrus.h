@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define ORTHRUS_ABI_VERSION 1
+#define ORTHRUS_ABI_VERSION 2
 
 typedef enum {
   ORTHRUS_OK = 0,
@@ -108,25 +108,34 @@ int32_t orthrus_verify_attn(const orthrus_attn_desc_t* desc, const void* q, cons
 /* ------------------------------------------------------------------------------------------
  * LM head with fused token choice (sec. 四 steps 1-2: each pass yields one token per slot).
  *   h [rows, hidden], w [vocab, hidden] (dtype); z = h w^T accumulated in fp32.
- *   temperature == 0: token_out[r] = argmax_x z[r, x], exact ties -> lowest id.
- *   temperature  > 0: token_out[r] = argmax_x (z[r,x]/T - ln(-ln u[r,x])) (Gumbel-max, a sample
- *     of softmax(z/T)); u from Philox4x64-10 with key (seed, stream_id) and, for row
- *     r = b*block + s, counter (s/4, x, round[b], seq_id[b]) and output word s%4; the
- *     uniform is ((word >> 41) + 0.5) * 2^-23.
+ *   sample == 0: token_out[r] = argmax_x z[r, x], exact ties -> lowest id (any temperature).
+ *   sample == 1 (needs temperature > 0): token_out[r] = argmax_x (z[r,x]/T - ln(-ln u[r,x]))
+ *     (Gumbel-max, a sample of softmax(z/T)); u from Philox4x64-10 with key (seed, stream_id)
+ *     and, for row r = b*block + s, counter (s/4, x, round[b], seq_id[b]) and output word s%4;
+ *     the uniform is ((word >> 41) + 0.5) * 2^-23.
  *   logits_out [rows, vocab] fp32 (optional, may be NULL): z.
- *   lse_out [rows] fp32 (optional): logsumexp_x(z[r,x] / T) (T = 1 when temperature == 0).
- *   seq_id, round [rows / block] int32: required when temperature > 0, else may be NULL.
+ *   lse_out [rows] fp32 (optional, may be NULL): logsumexp_x(z[r,x] / T) (T = 1 when
+ *     temperature == 0).  Computed only when asked for: each 32-column group's maximum and sum
+ *     of exp(z/T - max) are reduced by a fixed lane butterfly, and the groups of a row are merged
+ *     in an order set by vocab alone, so a row's lse has the same bits whatever rows share the
+ *     call.  Without lse_out the kernel reduces the token choice only.
+ *   seq_id, round [rows / block] int32: required when sample == 1, else may be NULL.
+ * The rejection accept reads the draft pass's logits and lse of a sampled call (sample == 1) and
+ * the verify pass's logits and lse of an argmax call at the same temperature (sample == 0).
  * Supported: dtype bf16 or fp32; hidden % 64 == 0.
+ * Workspace: orthrus_lmhead_workspace_bytes() bytes, caller-owned, contents undefined on entry
+ * and exit; calls that overlap on one workspace race.
  * ------------------------------------------------------------------------------------------ */
 typedef struct {
   int32_t rows;
   int32_t hidden;
   int32_t vocab;
   int32_t dtype;
-  int32_t block;       /* rows per sequence (RNG counters); rows % block == 0 */
-  int32_t stream_id;   /* ORTHRUS_STREAM_DRAFT or ORTHRUS_STREAM_AR             */
-  float temperature;
+  int32_t block;       /* rows per sequence (RNG counters); rows % block == 0 when sampling */
+  int32_t stream_id;   /* ORTHRUS_STREAM_DRAFT or ORTHRUS_STREAM_AR                         */
+  float temperature;   /* >= 0; scales the logsumexp and the Gumbel-max key                  */
   uint64_t seed;
+  int32_t sample;      /* 1: Gumbel-max sample, 0: argmax                                    */
 } orthrus_lmhead_desc_t;
 
 size_t orthrus_lmhead_workspace_bytes(const orthrus_lmhead_desc_t* desc);
@@ -165,17 +174,16 @@ int32_t orthrus_consensus_commit(int32_t batch, int32_t block, const int32_t* dr
  * seq_id[b]), word i%4).  At the first rejection j the token is drawn from max(0, p_j - q_j)
  * (from p_j if that has no mass) by exponential race argmax_x r(x) / E_x, E_x = -ln u_x with
  * u_x from (seed, RESID), counter (x/4, 0, round[b], seq_id[b]), word x%4; ties -> lowest id.
- * Then the same commit as orthrus_consensus_commit.
+ * A draft id outside [0, vocab) is rejected at its slot without reading its logits.
+ * Then the same commit as orthrus_consensus_commit.  One workgroup per sequence; no workspace.
  * ------------------------------------------------------------------------------------------ */
-size_t orthrus_rejection_workspace_bytes(int32_t batch);
 int32_t orthrus_rejection_accept(int32_t batch, int32_t block, int32_t vocab, float temperature,
                                  uint64_t seed, const int32_t* seq_id, const float* draft_logits,
                                  const float* target_logits, const float* draft_lse,
                                  const float* target_lse, const int32_t* draft, int32_t* ctx_len,
                                  int32_t* anchor, int32_t* accept, int32_t* out_tokens,
                                  int32_t* out_len, int32_t* round, int32_t* done, int32_t max_out,
-                                 int32_t max_ctx, void* workspace, size_t workspace_bytes,
-                                 void* stream);
+                                 int32_t max_ctx, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * Support kernels for the decoder layers of both views.

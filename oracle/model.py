@@ -117,6 +117,24 @@ def verify_attention(q, k_all, v_all, n, scale):
     return out
 
 
+def grouped_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, allowed: np.ndarray,
+                      scale: float) -> np.ndarray:
+    """The same attention as ``softmax_attend`` row by row, written with matrix products for
+    many rows at once: q [R, Hq, D] against k/v [N, Hkv, D] (query head h reads kv head h // G),
+    row r seeing the keys marked in ``allowed [R, N]``.  Returns [R, Hq, D]."""
+    R, Hq, D = q.shape
+    G = Hq // k.shape[1]
+    out = np.empty_like(q)
+    neg = np.where(allowed, 0.0, -np.inf).astype(q.dtype)
+    for h in range(Hq):
+        s = (q[:, h] @ k[:, h // G].T) * q.dtype.type(scale) + neg
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p = p / p.sum(axis=1, keepdims=True)
+        out[:, h] = p @ v[:, h // G]
+    return out
+
+
 def _linear(x: np.ndarray, w: np.ndarray, rowwise: bool) -> np.ndarray:
     """x [m, in] times w[out, in]^T."""
     if not rowwise:

@@ -37,7 +37,7 @@ class AttnDesc(ctypes.Structure):
 class LmHeadDesc(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int32), ("hidden", ctypes.c_int32), ("vocab", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("block", ctypes.c_int32), ("stream_id", ctypes.c_int32),
-                ("temperature", ctypes.c_float), ("seed", ctypes.c_uint64)]
+                ("temperature", ctypes.c_float), ("seed", ctypes.c_uint64), ("sample", ctypes.c_int32)]
 
 
 _lib = None
@@ -55,9 +55,8 @@ _SIGS = {
     "orthrus_consensus_commit": ([_I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P], _I32),
     "orthrus_draft_fill": ([_I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _I32, _I32, _P, _P, _P], _I32),
     "orthrus_draft_merge": ([_I32, _I32, _P, _P, _P, _P, _P], _I32),
-    "orthrus_rejection_workspace_bytes": ([_I32], _SZ),
     "orthrus_rejection_accept": ([_I32, _I32, _I32, _F32, _U64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                  _P, _P, _I32, _I32, _P, _SZ, _P], _I32),
+                                  _P, _P, _I32, _I32, _P], _I32),
     "orthrus_gemm_workspace_bytes": ([_I32, _I32, _I32, _I32, _I32], _SZ),
     "orthrus_gemm": ([_I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P], _I32),
     "orthrus_gemm_rope_kv_write": ([_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I32, _P,
@@ -135,8 +134,12 @@ def verify_attn(desc, q, k_pages, v_pages, page_table, ctx_len, out, ws, stream=
                                      0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
-def lmhead_desc(rows, hidden, vocab, dtype=BF16, block=32, stream_id=STREAM_DRAFT, temperature=0.0, seed=0):
-    return LmHeadDesc(rows, hidden, vocab, dtype, block, stream_id, temperature, seed)
+def lmhead_desc(rows, hidden, vocab, dtype=BF16, block=32, stream_id=STREAM_DRAFT, temperature=0.0, seed=0,
+                sample=None):
+    """``sample`` defaults to sampling exactly when ``temperature`` > 0."""
+    if sample is None:
+        sample = temperature > 0.0
+    return LmHeadDesc(rows, hidden, vocab, dtype, block, stream_id, temperature, seed, int(bool(sample)))
 
 
 def lmhead_workspace_bytes(desc: LmHeadDesc) -> int:
@@ -172,7 +175,7 @@ def rejection_accept(batch, block, vocab, temperature, seed, seq_id, draft_logit
     _check(lib().orthrus_rejection_accept(batch, block, vocab, temperature, seed, _ptr(seq_id), _ptr(draft_logits),
                                           _ptr(target_logits), _ptr(draft_lse), _ptr(target_lse), _ptr(draft),
                                           _ptr(ctx_len), _ptr(anchor), _ptr(accept), _ptr(out_tokens),
-                                          _ptr(out_len), _ptr(round_), _ptr(done), max_out, max_ctx, None, 0,
+                                          _ptr(out_len), _ptr(round_), _ptr(done), max_out, max_ctx,
                                           _stream(stream)))
 
 

@@ -87,10 +87,14 @@ __global__ __launch_bounds__(256) void rejection_kernel(int K, int V, float inv_
     if (lane < K) {
       d = draft[(size_t)b * K + lane];
       const size_t row = (size_t)b * K + lane;
-      const float q = expf(zd[row * V + d] * inv_t - lse_d[row]);
-      const float p = expf(zt[row * V + d] * inv_t - lse_t[row]);
-      const float u = philox_uniform(seed, ORTHRUS_STREAM_ACCEPT, lane, 0, rnd, sid);
-      acc = u * q < p;
+      if (d >= 0 && d < V) {
+        const float q = expf(zd[row * V + d] * inv_t - lse_d[row]);
+        const float p = expf(zt[row * V + d] * inv_t - lse_t[row]);
+        const float u = philox_uniform(seed, ORTHRUS_STREAM_ACCEPT, lane, 0, rnd, sid);
+        acc = u * q < p;
+      } else {
+        acc = false;  // an id outside the vocabulary is never accepted (and never read)
+      }
     }
     const uint64_t rej = __ballot(lane < K && !acc);
     k = rej ? __builtin_ctzll(rej) : K;
@@ -253,16 +257,13 @@ extern "C" int32_t orthrus_consensus_commit(int32_t batch, int32_t block, const 
   return check_launch("orthrus_consensus_commit");
 }
 
-extern "C" size_t orthrus_rejection_workspace_bytes(int32_t batch) { (void)batch; return 0; }
-
 extern "C" int32_t orthrus_rejection_accept(int32_t batch, int32_t block, int32_t vocab, float temperature,
                                             uint64_t seed, const int32_t* seq_id, const float* draft_logits,
                                             const float* target_logits, const float* draft_lse,
                                             const float* target_lse, const int32_t* draft, int32_t* ctx_len,
                                             int32_t* anchor, int32_t* accept, int32_t* out_tokens, int32_t* out_len,
                                             int32_t* round, int32_t* done, int32_t max_out, int32_t max_ctx,
-                                            void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace; (void)workspace_bytes;
+                                            void* stream) {
   if (int32_t s = check_state(batch, block, ctx_len, anchor, accept, out_tokens, out_len, round, done, max_out, max_ctx))
     return s;
   ORTHRUS_REQUIRE(vocab > 0 && temperature > 0.0f && std::isfinite(temperature), ORTHRUS_ERR_INVALID_ARG,

@@ -1,7 +1,7 @@
 // LM head with fused token choice: z = h W_lm^T on MFMA, and in the same kernel the per-tile
-// argmax (greedy) or Gumbel-max sample (temperature > 0), the per-tile logsumexp partials and
-// optionally the fp32 logits.  A second small kernel merges the per-tile partials of each row
-// in tile order (deterministic: no atomics, ties -> lowest id).
+// argmax or Gumbel-max sample, the per-32-column logsumexp partials when the caller asks for the
+// logsumexp, and optionally the fp32 logits.  A second small kernel merges the partials of each
+// row in a fixed order (deterministic: no atomics, ties -> lowest id).
 //
 // Orthrus paper summary (cjcn.com.cn), sec. 四: each pass turns the block rows into one token
 // per slot -- the diffusion view's candidates in step 1, the AR model's own choice in step 2.
@@ -16,13 +16,11 @@ struct LmArgs {
   const int32_t* seq_id;
   const int32_t* round;
   float* logits;
-  uint64_t* part_best;  // [rows, ntiles]
-  float* part_m;        // [rows, ntiles] max of z/T
-  float* part_s;        // [rows, ntiles] sum exp(z/T - max)
-  int32_t M, N, K, block, ntiles;
+  uint64_t* part_best;  // [rows, ntiles]  packed (key, id) maximum per 128-column tile
+  float2* part_lse;     // [rows, ngroups] (max, sum exp(. - max)) of z/T per 32-column group
+  int32_t M, N, K, block, ntiles, ngroups;
   int32_t tile0;        // first 128-column tile of this launch
-  float inv_t;          // 1/T (1 when greedy)
-  int32_t sample;       // temperature > 0
+  float inv_t;          // 1/T (1 when T == 0)
   uint64_t seed, stream_id;
 };
 
@@ -32,9 +30,24 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
   m = M;
 }
 
+// Merge (m2, s2) into (m, s) where either may be the empty partial (m = -inf).
+__device__ __forceinline__ void lse_merge_opt(float& m, float& s, float m2, float s2) {
+  if (m2 == -__builtin_huge_valf()) return;
+  if (m == -__builtin_huge_valf()) { m = m2; s = s2; return; }
+  lse_merge(m, s, m2, s2);
+}
+
 constexpr int kLmBN = 128;
 
-template <typename T, typename Cfg>
+// The epilogue per output element of a half-wave row:
+//  * token choice: the packed maximum of (key, id), key = z (greedy) or z/T - ln(-ln u) (Gumbel-max
+//    sample); reduced per 128-column tile, exact in any order;
+//  * optionally the logsumexp of z/T, in an order that does not depend on the tiling: for each
+//    32-column group (lane r holds column 32g + r in every tile layout) a 32-lane butterfly
+//    takes the group maximum, then the sum of exp(z/T - max); the finalize merges the groups of a
+//    row in an order fixed by the vocabulary size alone.  A row's logsumexp therefore has the same
+//    bits whatever M, the tile shape or the launch split.
+template <typename T, typename Cfg, bool kSample, bool kLse>
 __global__ __launch_bounds__(Cfg::NT) ORTHRUS_GEMM_WAVES void lmhead_kernel(LmArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int mtiles = (a.M + Cfg::BM - 1) / Cfg::BM;
@@ -42,6 +55,7 @@ __global__ __launch_bounds__(Cfg::NT) ORTHRUS_GEMM_WAVES void lmhead_kernel(LmAr
   xcd_tile_map(blockIdx.x, gridDim.x, 1, mtiles, sp, mt, nt);
   const int m0 = mt * Cfg::BM, n0 = a.tile0 * kLmBN + nt * Cfg::BN;
   constexpr int P = Cfg::BN / kLmBN, WPP = Cfg::WN / P;  // partial tiles per workgroup, waves per partial
+  constexpr int NG = Cfg::BN / 32;                        // 32-column groups per workgroup tile
   static_assert(P >= 1 && WPP >= 1 && P * kLmBN == Cfg::BN && WPP * P == Cfg::WN, "partials per 128 columns");
   f32x16 acc[Cfg::TM][Cfg::TN];
   gemm_mainloop<T, Cfg>(reinterpret_cast<const T*>(a.h), reinterpret_cast<const T*>(a.w), a.M, a.N, a.K, m0, n0, smem,
@@ -50,9 +64,9 @@ __global__ __launch_bounds__(Cfg::NT) ORTHRUS_GEMM_WAVES void lmhead_kernel(LmAr
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hh = lane >> 5, r = lane & 31;
   const int wm = w / Cfg::WN, wn = w % Cfg::WN;
   __syncthreads();  // LDS is reused below
-  uint64_t* red_best = reinterpret_cast<uint64_t*>(smem);                 // [BM][WN]
-  float* red_m = reinterpret_cast<float*>(red_best + Cfg::BM * Cfg::WN);  // [BM][WN]
-  float* red_s = red_m + Cfg::BM * Cfg::WN;
+  uint64_t* red_best = reinterpret_cast<uint64_t*>(smem);                   // [BM][WN]
+  float2* red_lse = reinterpret_cast<float2*>(red_best + Cfg::BM * Cfg::WN);  // [BM][NG]
+  constexpr float kNegInf = -__builtin_huge_valf();
 
 #pragma unroll
   for (int i = 0; i < Cfg::TM; ++i) {
@@ -61,41 +75,41 @@ __global__ __launch_bounds__(Cfg::NT) ORTHRUS_GEMM_WAVES void lmhead_kernel(LmAr
       const int mrow = (wm * Cfg::TM + i) * 32 + acc_row(e, hh);
       const int m = m0 + mrow;
       const bool mok = m < a.M;
-      int bseq = 0, slot = 0;
-      if (a.sample && mok) { bseq = m / a.block; slot = m % a.block; }
+      int32_t rnd = 0, sid = 0, slot = 0;
+      if (kSample && mok) {
+        const int bseq = m / a.block;
+        slot = m % a.block;
+        rnd = a.round[bseq];
+        sid = a.seq_id[bseq];
+      }
       uint64_t best = 0;
-      float lm = -__builtin_huge_valf(), ls = 0.0f;
 #pragma unroll
       for (int j = 0; j < Cfg::TN; ++j) {
         const int n = n0 + (wn * Cfg::TN + j) * 32 + r;
-        if (!mok || n >= a.N) continue;
+        const bool ok = mok && n < a.N;
         const float z = acc[i][j][e];
-        if (a.logits) a.logits[(size_t)m * a.N + n] = z;
-        const float zt = z * a.inv_t;
+        if (ok && a.logits) a.logits[(size_t)m * a.N + n] = z;
         float key = z;
-        if (a.sample) {
-          const float u = philox_uniform(a.seed, a.stream_id, slot, n, a.round[bseq], a.seq_id[bseq]);
-          key = zt - logf(-logf(u));
+        if constexpr (kSample) {
+          const float u = philox_uniform(a.seed, a.stream_id, slot, n, rnd, sid);
+          key = z * a.inv_t - logf(-logf(u));
         }
-        best = umax64(best, pack_argmax(key, n));
-        if (zt > lm) { ls = ls * expf(lm - zt) + 1.0f; lm = zt; }
-        else ls += expf(zt - lm);
-      }
-      // reduce over the 32 columns held by this half-wave (same rows), fixed pattern
+        if (ok) best = umax64(best, pack_argmax(key, n));
+        if constexpr (kLse) {
+          const float zt = ok ? z * a.inv_t : kNegInf;
+          float gm = zt;
 #pragma unroll
-      for (int off = 1; off < 32; off <<= 1) {
-        best = umax64(best, shfl_xor_u64(best, off));
-        const float m2 = shfl_xor_f(lm, off), s2 = shfl_xor_f(ls, off);
-        if (m2 != -__builtin_huge_valf()) {
-          if (lm == -__builtin_huge_valf()) { lm = m2; ls = s2; }
-          else lse_merge(lm, ls, m2, s2);
+          for (int off = 1; off < 32; off <<= 1) gm = fmaxf(gm, shfl_xor_f(gm, off));
+          float gs = ok ? expf(zt - gm) : 0.0f;
+#pragma unroll
+          for (int off = 1; off < 32; off <<= 1) gs += shfl_xor_f(gs, off);
+          if (r == 0) red_lse[mrow * NG + wn * Cfg::TN + j] = make_float2(gm, gs);
         }
       }
-      if (r == 0) {
-        red_best[mrow * Cfg::WN + wn] = best;
-        red_m[mrow * Cfg::WN + wn] = lm;
-        red_s[mrow * Cfg::WN + wn] = ls;
-      }
+      // reduce over the 32 columns held by this half-wave (same rows)
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) best = umax64(best, shfl_xor_u64(best, off));
+      if (r == 0) red_best[mrow * Cfg::WN + wn] = best;
     }
   }
   __syncthreads();
@@ -106,61 +120,64 @@ __global__ __launch_bounds__(Cfg::NT) ORTHRUS_GEMM_WAVES void lmhead_kernel(LmAr
     if (m >= a.M || tile >= a.ntiles) continue;
     const int q0 = mrow * Cfg::WN + pt * WPP;
     uint64_t best = red_best[q0];
-    float lm = red_m[q0], ls = red_s[q0];
-    for (int q = 1; q < WPP; ++q) {
-      best = umax64(best, red_best[q0 + q]);
-      const float m2 = red_m[q0 + q];
-      if (m2 != -__builtin_huge_valf()) {
-        if (lm == -__builtin_huge_valf()) { lm = m2; ls = red_s[q0 + q]; }
-        else lse_merge(lm, ls, m2, red_s[q0 + q]);
-      }
+    for (int q = 1; q < WPP; ++q) best = umax64(best, red_best[q0 + q]);
+    a.part_best[(size_t)m * a.ntiles + tile] = best;
+  }
+  if constexpr (kLse) {
+    // the tile's group partials: consecutive threads take consecutive groups of a row
+    const int g0 = n0 / 32;
+    for (int idx = threadIdx.x; idx < Cfg::BM * NG; idx += Cfg::NT) {
+      const int mrow = idx / NG, g = idx % NG;
+      const int m = m0 + mrow;
+      if (m >= a.M || g0 + g >= a.ngroups) continue;
+      a.part_lse[(size_t)m * a.ngroups + g0 + g] = red_lse[idx];
     }
-    const size_t o = (size_t)m * a.ntiles + tile;
-    a.part_best[o] = best;
-    a.part_m[o] = lm;
-    a.part_s[o] = ls;
   }
 }
 
-// One wavefront per row: merge the row's tile partials (strided by lane, then a fixed xor tree).
-__global__ __launch_bounds__(64) void lmhead_finalize(const uint64_t* part_best, const float* part_m, const float* part_s,
-                                                      int ntiles, int32_t* token, float* lse) {
+// One wavefront per row: the packed maxima of the row's tiles (exact in any order) and, when asked
+// for, the logsumexp of its 32-column groups merged lane-strided in group order, then by a fixed
+// xor butterfly: an order set by the vocabulary size alone.
+__global__ __launch_bounds__(64) void lmhead_finalize(const uint64_t* part_best, const float2* part_lse, int ntiles,
+                                                      int ngroups, int32_t* token, float* lse) {
   const int row = blockIdx.x, lane = threadIdx.x;
   uint64_t best = 0;
-  float lm = -__builtin_huge_valf(), ls = 0.0f;
-  auto merge = [&](uint64_t b2, float m2, float s2) {
-    best = umax64(best, b2);
-    if (m2 != -__builtin_huge_valf()) {
-      if (lm == -__builtin_huge_valf()) { lm = m2; ls = s2; }
-      else lse_merge(lm, ls, m2, s2);
-    }
-  };
-  // four of the lane's tiles are loaded before they are merged in tile order
-  constexpr int U = 4;
-  const size_t base = (size_t)row * ntiles;
-  int t = lane;
-  for (; t + 64 * (U - 1) < ntiles; t += 64 * U) {
-    uint64_t b2[U];
-    float m2[U], s2[U];
+  {
+    constexpr int U = 4;  // four of the lane's tiles are loaded before they are merged
+    const size_t base = (size_t)row * ntiles;
+    int t = lane;
+    for (; t + 64 * (U - 1) < ntiles; t += 64 * U) {
+      uint64_t b2[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const size_t o = base + t + 64 * u;
-      b2[u] = part_best[o];
-      m2[u] = part_m[o];
-      s2[u] = part_s[o];
-    }
-    __builtin_amdgcn_sched_barrier(0);
+      for (int u = 0; u < U; ++u) b2[u] = part_best[base + t + 64 * u];
 #pragma unroll
-    for (int u = 0; u < U; ++u) merge(b2[u], m2[u], s2[u]);
+      for (int u = 0; u < U; ++u) best = umax64(best, b2[u]);
+    }
+    for (; t < ntiles; t += 64) best = umax64(best, part_best[base + t]);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) best = umax64(best, shfl_xor_u64(best, off));
   }
-  for (; t < ntiles; t += 64) merge(part_best[base + t], part_m[base + t], part_s[base + t]);
+  float lm = -__builtin_huge_valf(), ls = 0.0f;
+  if (part_lse) {
+    constexpr int U = 4;
+    const size_t base = (size_t)row * ngroups;
+    int g = lane;
+    for (; g + 64 * (U - 1) < ngroups; g += 64 * U) {
+      float2 p2[U];
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    best = umax64(best, shfl_xor_u64(best, off));
-    const float m2 = shfl_xor_f(lm, off), s2 = shfl_xor_f(ls, off);
-    if (m2 != -__builtin_huge_valf()) {
-      if (lm == -__builtin_huge_valf()) { lm = m2; ls = s2; }
-      else lse_merge(lm, ls, m2, s2);
+      for (int u = 0; u < U; ++u) p2[u] = part_lse[base + g + 64 * u];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < U; ++u) lse_merge_opt(lm, ls, p2[u].x, p2[u].y);
+    }
+    for (; g < ngroups; g += 64) {
+      const float2 p2 = part_lse[base + g];
+      lse_merge_opt(lm, ls, p2.x, p2.y);
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float m2 = shfl_xor_f(lm, off), s2 = shfl_xor_f(ls, off);
+      lse_merge_opt(lm, ls, m2, s2);
     }
   }
   if (lane == 0) {
@@ -169,16 +186,24 @@ __global__ __launch_bounds__(64) void lmhead_finalize(const uint64_t* part_best,
   }
 }
 
+template <typename T, typename Cfg, bool kSample, bool kLse>
+int32_t launch_mode(const LmArgs& a, hipStream_t st, int grid, size_t lds) {
+  allow_lds(lmhead_kernel<T, Cfg, kSample, kLse>, lds);
+  hipLaunchKernelGGL((lmhead_kernel<T, Cfg, kSample, kLse>), dim3(grid), dim3(Cfg::NT), lds, st, a);
+  return check_launch("orthrus_lmhead_argmax");
+}
+
 template <typename T, typename Cfg>
-int32_t launch(LmArgs& a, hipStream_t st, int tile0 = 0, int wg_tiles = -1) {
+int32_t launch(LmArgs& a, bool sample, bool lse, hipStream_t st, int tile0 = 0, int wg_tiles = -1) {
   const int mtiles = (a.M + Cfg::BM - 1) / Cfg::BM;
-  const size_t lds = std::max(Cfg::RING, (size_t)Cfg::BM * Cfg::WN * 16);
+  const size_t red = (size_t)Cfg::BM * Cfg::WN * sizeof(uint64_t) + (size_t)Cfg::BM * (Cfg::BN / 32) * sizeof(float2);
+  const size_t lds = std::max(Cfg::RING, red);
   if (wg_tiles < 0) wg_tiles = (a.ntiles - tile0) / (Cfg::BN / kLmBN) + ((a.ntiles - tile0) % (Cfg::BN / kLmBN) != 0);
   if (wg_tiles == 0) return ORTHRUS_OK;
   a.tile0 = tile0;
-  allow_lds(lmhead_kernel<T, Cfg>, lds);
-  hipLaunchKernelGGL((lmhead_kernel<T, Cfg>), dim3(mtiles * wg_tiles), dim3(Cfg::NT), lds, st, a);
-  return check_launch("orthrus_lmhead_argmax");
+  const int grid = mtiles * wg_tiles;
+  if (sample) return lse ? launch_mode<T, Cfg, true, true>(a, st, grid, lds) : launch_mode<T, Cfg, true, false>(a, st, grid, lds);
+  return lse ? launch_mode<T, Cfg, false, true>(a, st, grid, lds) : launch_mode<T, Cfg, false, false>(a, st, grid, lds);
 }
 
 #ifndef ORTHRUS_LM_BIG_CFG
@@ -199,7 +224,7 @@ template <typename T> using LmPairCfg = GemmCfg<T, 256, 256, 4, 2, 2, 2, true>;
 // 256x256 tiles would leave a last wave of 82 workgroups on 256 CUs at V = 151936, hence the mix.
 // The partials stay per 128-column tile, so the finalize merge is the same whatever the split.
 template <typename T>
-int32_t launch_mixed(LmArgs& a, hipStream_t st) {
+int32_t launch_mixed(LmArgs& a, bool sample, bool lse, hipStream_t st) {
   static int cus = 0;
   if (cus == 0) {
     int dev = 0;
@@ -209,8 +234,8 @@ int32_t launch_mixed(LmArgs& a, hipStream_t st) {
   const int mtiles = (a.M + 255) / 256;
   const int rounds = (a.ntiles * mtiles) / (2 * cus);
   int npairs = std::min(a.ntiles / 2, rounds * cus / mtiles);
-  if (int32_t s = launch<T, LmPairCfg<T>>(a, st, 0, npairs)) return s;
-  return launch<T, ORTHRUS_LM_HUGE_CFG(T)>(a, st, 2 * npairs);
+  if (int32_t s = launch<T, LmPairCfg<T>>(a, sample, lse, st, 0, npairs)) return s;
+  return launch<T, ORTHRUS_LM_HUGE_CFG(T)>(a, sample, lse, st, 2 * npairs);
 }
 
 }  // namespace
@@ -218,10 +243,12 @@ int32_t launch_mixed(LmArgs& a, hipStream_t st) {
 
 using namespace orthrus;
 
+// Workspace: the packed maxima of every (row, 128-column tile), then the logsumexp partials of
+// every (row, 32-column group).
 extern "C" size_t orthrus_lmhead_workspace_bytes(const orthrus_lmhead_desc_t* d) {
   if (!d || d->rows < 0 || d->vocab <= 0) return 0;
-  const size_t ntiles = (d->vocab + kLmBN - 1) / kLmBN;
-  return (size_t)d->rows * ntiles * (sizeof(uint64_t) + 2 * sizeof(float));
+  const size_t ntiles = (d->vocab + kLmBN - 1) / kLmBN, ngroups = (d->vocab + 31) / 32;
+  return (size_t)d->rows * (ntiles * sizeof(uint64_t) + ngroups * sizeof(float2));
 }
 
 extern "C" int32_t orthrus_lmhead_argmax(const orthrus_lmhead_desc_t* d, const void* h, const void* w,
@@ -233,8 +260,10 @@ extern "C" int32_t orthrus_lmhead_argmax(const orthrus_lmhead_desc_t* d, const v
   ORTHRUS_REQUIRE(valid_dtype(d->dtype), ORTHRUS_ERR_INVALID_ARG, "lmhead: bad dtype");
   ORTHRUS_REQUIRE(d->temperature >= 0.0f && std::isfinite(d->temperature), ORTHRUS_ERR_INVALID_ARG,
                   "lmhead: temperature must be finite and >= 0");
+  ORTHRUS_REQUIRE(d->sample == 0 || d->sample == 1, ORTHRUS_ERR_INVALID_ARG, "lmhead: sample must be 0 or 1");
   ORTHRUS_REQUIRE(h && w && token_out, ORTHRUS_ERR_INVALID_ARG, "lmhead: null pointer");
-  const bool sample = d->temperature > 0.0f;
+  const bool sample = d->sample != 0;
+  ORTHRUS_REQUIRE(!sample || d->temperature > 0.0f, ORTHRUS_ERR_INVALID_ARG, "lmhead: sampling needs temperature > 0");
   ORTHRUS_REQUIRE(!sample || (seq_id && round && d->block > 0 && d->rows % d->block == 0), ORTHRUS_ERR_INVALID_ARG,
                   "lmhead: sampling needs seq_id, round and rows %% block == 0");
   const size_t need = orthrus_lmhead_workspace_bytes(d);
@@ -245,29 +274,29 @@ extern "C" int32_t orthrus_lmhead_argmax(const orthrus_lmhead_desc_t* d, const v
   a.h = h; a.w = w; a.seq_id = seq_id; a.round = round; a.logits = logits_out;
   a.M = d->rows; a.N = d->vocab; a.K = d->hidden; a.block = d->block > 0 ? d->block : 1;
   a.ntiles = (d->vocab + kLmBN - 1) / kLmBN;
+  a.ngroups = (d->vocab + 31) / 32;
   a.part_best = reinterpret_cast<uint64_t*>(ws);
-  a.part_m = reinterpret_cast<float*>(a.part_best + (size_t)a.M * a.ntiles);
-  a.part_s = a.part_m + (size_t)a.M * a.ntiles;
-  a.inv_t = sample ? 1.0f / d->temperature : 1.0f;
-  a.sample = sample;
+  a.part_lse = reinterpret_cast<float2*>(a.part_best + (size_t)a.M * a.ntiles);
+  a.inv_t = d->temperature > 0.0f ? 1.0f / d->temperature : 1.0f;
   a.seed = d->seed;
   a.stream_id = (uint64_t)d->stream_id;
+  const bool lse = lse_out != nullptr;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   int32_t s;
   if (d->dtype == ORTHRUS_BF16) {
-    if (a.M <= 32) s = launch<bf16, GemmCfg<bf16, 32, kLmBN, 1, 4, 4, 4>>(a, st);
-    else if (a.M <= 64) s = launch<bf16, GemmCfg<bf16, 64, kLmBN, 2, 2, 3, 3>>(a, st);
-    else if (a.M <= 128) s = launch<bf16, ORTHRUS_LM_BIG_CFG(bf16)>(a, st);
-    else if (a.K % 128 == 0) s = launch_mixed<bf16>(a, st);
-    else s = launch<bf16, ORTHRUS_LM_HUGE_CFG(bf16)>(a, st);
+    if (a.M <= 32) s = launch<bf16, GemmCfg<bf16, 32, kLmBN, 1, 4, 4, 4>>(a, sample, lse, st);
+    else if (a.M <= 64) s = launch<bf16, GemmCfg<bf16, 64, kLmBN, 2, 2, 3, 3>>(a, sample, lse, st);
+    else if (a.M <= 128) s = launch<bf16, ORTHRUS_LM_BIG_CFG(bf16)>(a, sample, lse, st);
+    else if (a.K % 128 == 0) s = launch_mixed<bf16>(a, sample, lse, st);
+    else s = launch<bf16, ORTHRUS_LM_HUGE_CFG(bf16)>(a, sample, lse, st);
   } else {
-    if (a.M <= 32) s = launch<float, GemmCfg<float, 32, kLmBN, 1, 4, 4, 4>>(a, st);
-    else if (a.M <= 64) s = launch<float, GemmCfg<float, 64, kLmBN, 2, 2, 3, 3>>(a, st);
-    else if (a.M <= 128) s = launch<float, ORTHRUS_LM_BIG_CFG(float)>(a, st);
-    else s = launch<float, ORTHRUS_LM_HUGE_CFG(float)>(a, st);
+    if (a.M <= 32) s = launch<float, GemmCfg<float, 32, kLmBN, 1, 4, 4, 4>>(a, sample, lse, st);
+    else if (a.M <= 64) s = launch<float, GemmCfg<float, 64, kLmBN, 2, 2, 3, 3>>(a, sample, lse, st);
+    else if (a.M <= 128) s = launch<float, ORTHRUS_LM_BIG_CFG(float)>(a, sample, lse, st);
+    else s = launch<float, ORTHRUS_LM_HUGE_CFG(float)>(a, sample, lse, st);
   }
   if (s != ORTHRUS_OK) return s;
-  hipLaunchKernelGGL(lmhead_finalize, dim3(a.M), dim3(64), 0, st, a.part_best, a.part_m, a.part_s, a.ntiles, token_out,
-                     lse_out);
+  hipLaunchKernelGGL(lmhead_finalize, dim3(a.M), dim3(64), 0, st, a.part_best, lse ? a.part_lse : nullptr, a.ntiles,
+                     a.ngroups, token_out, lse_out);
   return check_launch("orthrus_lmhead_argmax(finalize)");
 }

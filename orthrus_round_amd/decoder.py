@@ -183,11 +183,12 @@ class Decoder:
             L.gemm(M, 2 * I, H, dt, dt, L.EPI_SWIGLU, a, Wl["gate_up"], None, self.h, self.gemm_ws)
             L.gemm_residual_rmsnorm(M, H, I, dt, self.h, Wl["down"], x, nxt, s.eps, a, self.gemm_ws)
 
-    def _lm_head(self, nb, kb, tokens, temperature=0.0, seed=0, stream_id=L.STREAM_DRAFT, logits=None, lse=None):
+    def _lm_head(self, nb, kb, tokens, temperature=0.0, seed=0, stream_id=L.STREAM_DRAFT, logits=None, lse=None,
+                 sample=None):
         s = self.shape
         M = nb * kb
         # self.a[:M] already holds final_norm(x): the last layer's down projection wrote it
-        d = L.lmhead_desc(M, s.hidden, s.vocab, self.dt, kb, stream_id, temperature, seed)
+        d = L.lmhead_desc(M, s.hidden, s.vocab, self.dt, kb, stream_id, temperature, seed, sample)
         L.lmhead_argmax(d, self.a[:M], self.lm_head, self.seq_id, self.round, tokens, logits, lse, self.lm_ws)
 
     # ------------------------------------------------------------------ prefill / state
@@ -312,23 +313,24 @@ class Decoder:
         self._lm_head(B, K, self.draft, temperature, seed, L.STREAM_DRAFT, self._logits[0], self._lse[0])
         L.embed_block(B, K, s.hidden, self.dt, self.embed, self.anchor, self.draft, K, 0, s.mask_id, self.x)
         self._layers("ar", B, K, self.ctx_len, draft=False)
-        self._lm_head(B, K, self.target, temperature, seed, L.STREAM_AR, self._logits[1], self._lse[1])
+        # the verify pass keeps its logits and lse(z/T) for the accept test; it draws no sample
+        self._lm_head(B, K, self.target, temperature, seed, L.STREAM_AR, self._logits[1], self._lse[1], sample=False)
         L.rejection_accept(B, K, s.vocab, temperature, seed, self.seq_id, self._logits[0], self._logits[1],
                            self._lse[0], self._lse[1], self.draft, self.ctx_len, self.anchor, self.accept,
                            self.out_tokens, self.out_len, self.round, self.done, self.max_out, self.max_ctx)
 
     def ar_step(self, temperature: float = 0.0, seed: int = 0, logits: torch.Tensor | None = None):
         """One plain AR step for every sequence: a one-row causal pass, argmax/sample, commit.
-        With `logits` (fp32 [batch, vocab]) the step also writes the LM head's logits there."""
+        With `logits` (fp32 [batch, vocab]) the step also writes the LM head's logits there.
+        Returns the step's tokens as a [batch, 1] view of a buffer the next call overwrites."""
         B, s = self.B, self.shape
         L.embed_block(B, 1, s.hidden, self.dt, self.embed, self.anchor, None, 0, 0, s.mask_id, self.x)
         self._layers("ar", B, 1, self.ctx_len, draft=False)
-        tok = self.target[:, :1]
         t_flat = self.target.view(-1)[:B]
         self._lm_head(B, 1, t_flat, temperature, seed, L.STREAM_AR, logits=logits)
         L.consensus_commit(B, 1, t_flat, t_flat, self.ctx_len, self.anchor, self.accept, self.out_tokens,
                            self.out_len, self.round, self.done, self.max_out, self.max_ctx)
-        return tok
+        return t_flat.view(B, 1)
 
     # ------------------------------------------------------------------ graphs
     def capture(self, fn, *args):

@@ -36,8 +36,10 @@ def test_abi_version_matches_header():
 
 def test_struct_layouts_match_header():
     # orthrus_attn_desc_t: 11 int32 + float; orthrus_lmhead_desc_t: 6 int32 + float + pad + uint64
+    # + int32 + pad
     assert ctypes.sizeof(_lib.AttnDesc) == 48
-    assert ctypes.sizeof(_lib.LmHeadDesc) == 40 and _lib.LmHeadDesc.seed.offset == 32
+    assert ctypes.sizeof(_lib.LmHeadDesc) == 48 and _lib.LmHeadDesc.seed.offset == 32
+    assert _lib.LmHeadDesc.sample.offset == 40
 
 
 @pytest.mark.parametrize("call,status", [

@@ -123,17 +123,35 @@ def qwen3_8b_batch():
     return synth.attn_inputs(3, ctx, 32, 8, 128)
 
 
+def oracle_attn_all_heads(inp, b, K, draft):
+    """Every query head of sequence b in the oracle's matrix-product form (pinned to the row form
+    and to SDPA on the CPU)."""
+    n = int(inp.ctx[b])
+    k, v = inp.kv[b]
+    q = inp.q[b, :K].astype(np.float64)
+    if draft:
+        kk = np.concatenate([k[:n], inp.k_blk[b, :K]]).astype(np.float64)
+        vv = np.concatenate([v[:n], inp.v_blk[b, :K]]).astype(np.float64)
+        allowed = np.ones((K, n + K), bool)
+    else:
+        kk, vv = k[: n + K].astype(np.float64), v[: n + K].astype(np.float64)
+        allowed = np.ones((K, n + K), bool)
+        allowed[:, n:] = np.tril(np.ones((K, K), bool))
+    return M.grouped_attention(q, kk, vv, allowed, inp.scale)
+
+
 @pytest.mark.parametrize("draft", [True, False])
 def test_qwen3_8b_batched_paged_ragged(qwen3_8b_batch, draft):
+    """Every sequence, every query head (all 8 kv heads) of the batched paged workload."""
     inp = qwen3_8b_batch
     g = run_attn(inp, 32, 8, 128, 32, draft, kv_chunk=1024)
-    rs = np.random.default_rng(1)
+    worst = 0.0
     for b in range(16):
-        hk = int(rs.integers(0, 8))
-        heads = [4 * hk + j for j in range(4)]
-        o = oracle_attn(inp, b, 32, draft, heads=heads)
-        err = normwise(g[b][:, heads], o)
-        assert err <= 2e-3, (b, hk, err)
+        o = oracle_attn_all_heads(inp, b, 32, draft)
+        err = normwise(g[b], o)
+        worst = max(worst, err)
+        assert err <= 2e-3, (b, err)
+    print(f"draft={draft} worst normwise err over 16 x 32 heads {worst:.2e}")
 
 
 def test_page_order_is_invisible(qwen3_8b_batch):

@@ -125,3 +125,13 @@ def test_sampled_ar_matches_oracle(tiny, prompts):
     dec = make(W)
     toks, _ = dec.generate_ar(prompts[:1], 48, temperature=0.8, seed=7)
     assert list(toks[0]) == Dc.generate_ar(Wt, prompts[0], 48, temperature=0.8, seed=7)
+
+
+def test_ar_step_returns_each_sequences_token(tiny, prompts):
+    """ar_step's return value holds every sequence's own token of that step."""
+    W, _ = tiny
+    dec = make(W, B=4)
+    dec.prefill(torch.as_tensor(prompts), 6)
+    for step in range(6):
+        tok = dec.ar_step().cpu().numpy()[:, 0]
+        assert np.array_equal(tok, dec.out_tokens[:, step].cpu().numpy()), step

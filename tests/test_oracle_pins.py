@@ -146,6 +146,27 @@ def test_masked_attention_matches_sdpa_random_mask():
     np.testing.assert_allclose(M.masked_attention(q, k, v, mask, 0.2), _sdpa(q, k, v, mask, 0.2), rtol=1e-12, atol=1e-12)
 
 
+@pytest.mark.parametrize("n", [0, 40])
+def test_grouped_attention_matches_sdpa_and_row_form(n):
+    """The matrix-product form gives the draft and verify attention of the row-by-row oracle and
+    of torch's SDPA with the explicit masks, with G = 4 query heads per kv head."""
+    rs = np.random.default_rng(30 + n)
+    K, Hq, Hkv, D = 8, 8, 2, 16
+    q = rs.standard_normal((K, Hq, D))
+    k, v = rs.standard_normal((2, n + K, Hkv, D))
+    kb, vb = rs.standard_normal((2, K, Hkv, D))
+    draft = M.grouped_attention(q, np.concatenate([k[:n], kb]), np.concatenate([v[:n], vb]),
+                                np.ones((K, n + K), bool), 0.3)
+    np.testing.assert_allclose(draft, M.draft_attention(q, k[:n], v[:n], kb, vb, 0.3), rtol=1e-12, atol=1e-12)
+    causal = np.ones((K, n + K), bool)
+    causal[:, n:] = np.tril(np.ones((K, K), bool))
+    ver = M.grouped_attention(q, k, v, causal, 0.3)
+    np.testing.assert_allclose(ver, M.verify_attention(q, k, v, n, 0.3), rtol=1e-12, atol=1e-12)
+    for h in range(Hq):
+        np.testing.assert_allclose(ver[:, h], _sdpa(q[:, h], k[:, h // 4], v[:, h // 4], causal, 0.3),
+                                   rtol=1e-12, atol=1e-12)
+
+
 # --------------------------------------------------------------------------- decoder vs transformers Llama
 
 def _llama(W, shape):
