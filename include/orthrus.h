@@ -144,6 +144,22 @@ int32_t orthrus_lmhead_argmax(const orthrus_lmhead_desc_t* desc, const void* h, 
                               float* logits_out, float* lse_out, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/* orthrus_lmhead_argmax without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * The partials live in a static device array of ORTHRUS_LMHEAD_SCRATCH_BYTES (32 MiB) that each
+ * GPU the library runs on holds until the process ends; the call allocates nothing.  It serves
+ * calls whose orthrus_lmhead_workspace_bytes() is at most that size (e.g. 512 rows at vocabulary
+ * 151936); larger ones return ORTHRUS_ERR_WORKSPACE before anything is launched.  The device is
+ * the stream's (the current device for the null stream).  Every call on one GPU shares its array:
+ * calls that overlap on one GPU (several streams, several threads) race; calls in stream order do
+ * not.  Nothing in the array needs clearing between calls (every partial read is written first
+ * by the same call).  Results have the bits of orthrus_lmhead_argmax with the same arguments. */
+#define ORTHRUS_LMHEAD_SCRATCH_BYTES (32u << 20)
+int32_t orthrus_lmhead_argmax_noalloc(const orthrus_lmhead_desc_t* desc, const void* h,
+                                      const void* w, const int32_t* seq_id, const int32_t* round,
+                                      int32_t* token_out, float* logits_out, float* lse_out,
+                                      void* stream);
+
 /* ------------------------------------------------------------------------------------------
  * Greedy consensus + commit (sec. 四 step 3), one wavefront per sequence, no host round-trip.
  *   draft [batch, block]  = d_1..d_K (diffusion view's choice for positions n+1..n+K)

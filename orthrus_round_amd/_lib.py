@@ -52,6 +52,7 @@ _SIGS = {
     "orthrus_verify_attn": ([ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I32),
     "orthrus_lmhead_workspace_bytes": ([ctypes.POINTER(LmHeadDesc)], _SZ),
     "orthrus_lmhead_argmax": ([ctypes.POINTER(LmHeadDesc), _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I32),
+    "orthrus_lmhead_argmax_noalloc": ([ctypes.POINTER(LmHeadDesc), _P, _P, _P, _P, _P, _P, _P, _P], _I32),
     "orthrus_consensus_commit": ([_I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P], _I32),
     "orthrus_draft_fill": ([_I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _I32, _I32, _P, _P, _P], _I32),
     "orthrus_draft_merge": ([_I32, _I32, _P, _P, _P, _P, _P], _I32),
@@ -150,6 +151,11 @@ def lmhead_argmax(desc, h, w, seq_id, round_, token_out, logits_out, lse_out, ws
     _check(lib().orthrus_lmhead_argmax(ctypes.byref(desc), _ptr(h), _ptr(w), _ptr(seq_id), _ptr(round_),
                                        _ptr(token_out), _ptr(logits_out), _ptr(lse_out), _ptr(ws),
                                        ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def lmhead_argmax_noalloc(desc, h, w, seq_id, round_, token_out, logits_out, lse_out, stream=None):
+    _check(lib().orthrus_lmhead_argmax_noalloc(ctypes.byref(desc), _ptr(h), _ptr(w), _ptr(seq_id), _ptr(round_),
+                                               _ptr(token_out), _ptr(logits_out), _ptr(lse_out), _stream(stream)))
 
 
 def consensus_commit(batch, block, draft, target, ctx_len, anchor, accept, out_tokens, out_len, round_, done,

@@ -5,6 +5,8 @@
 //
 // Orthrus paper summary (cjcn.com.cn), sec. 四: each pass turns the block rows into one token
 // per slot -- the diffusion view's candidates in step 1, the AR model's own choice in step 2.
+#include <mutex>
+
 #include "gemm_core.hpp"
 
 namespace orthrus {
@@ -299,4 +301,62 @@ extern "C" int32_t orthrus_lmhead_argmax(const orthrus_lmhead_desc_t* d, const v
   hipLaunchKernelGGL(lmhead_finalize, dim3(a.M), dim3(64), 0, st, a.part_best, lse ? a.part_lse : nullptr, a.ntiles,
                      a.ngroups, token_out, lse_out);
   return check_launch("orthrus_lmhead_argmax(finalize)");
+}
+
+// ------------------------------------------------------------------------------------------
+// The same call with its partials in a static device array instead of a caller workspace, for
+// callers that cannot allocate.  Each device holds its own copy of `scratch` from the module load
+// until the process ends; its address on a device is taken once with hipGetSymbolAddress (with
+// that device current) and kept per device, since the host-side name is not a device address.
+// ------------------------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[ORTHRUS_LMHEAD_SCRATCH_BYTES];
+
+namespace orthrus {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int32_t scratch_address(hipStream_t st, void** out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return fail(ORTHRUS_ERR_HIP, "lmhead_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  int dev = cur;
+  if (st != nullptr) {
+    e = hipStreamGetDevice(st, &dev);
+    if (e != hipSuccess) return fail(ORTHRUS_ERR_HIP, "lmhead_noalloc: hipStreamGetDevice: %s", hipGetErrorString(e));
+  }
+  ORTHRUS_REQUIRE(dev >= 0 && dev < kMaxDevices, ORTHRUS_ERR_UNSUPPORTED, "lmhead_noalloc: device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(ORTHRUS_ERR_HIP, "lmhead_noalloc: hipSetDevice(%d): %s", dev, hipGetErrorString(e));
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || p == nullptr)
+      return fail(ORTHRUS_ERR_HIP, "lmhead_noalloc: hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ORTHRUS_OK;
+}
+
+}  // namespace
+}  // namespace orthrus
+
+extern "C" int32_t orthrus_lmhead_argmax_noalloc(const orthrus_lmhead_desc_t* d, const void* h, const void* w,
+                                                 const int32_t* seq_id, const int32_t* round, int32_t* token_out,
+                                                 float* logits_out, float* lse_out, void* stream) {
+  ORTHRUS_REQUIRE(d != nullptr, ORTHRUS_ERR_INVALID_ARG, "lmhead_noalloc: null descriptor");
+  const size_t need = orthrus_lmhead_workspace_bytes(d);
+  ORTHRUS_REQUIRE(need <= (size_t)ORTHRUS_LMHEAD_SCRATCH_BYTES, ORTHRUS_ERR_WORKSPACE,
+                  "lmhead_noalloc: %d rows x vocab %d need %zu bytes of partials, above the static scratch of %zu",
+                  d->rows, d->vocab, need, (size_t)ORTHRUS_LMHEAD_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (int32_t s = scratch_address(reinterpret_cast<hipStream_t>(stream), &ws)) return s;
+  return orthrus_lmhead_argmax(d, h, w, seq_id, round, token_out, logits_out, lse_out, ws,
+                               (size_t)ORTHRUS_LMHEAD_SCRATCH_BYTES, stream);
 }
