@@ -41,6 +41,10 @@ def parse():
     p.add_argument("--match-tokens", type=int, default=64)
     p.add_argument("--control-chunk", type=int, default=1024,
                    help="kv_chunk of the divergence control runs (another key summation order)")
+    p.add_argument("--only", choices=["attn-c3"], default=None,
+                   help="run one workload alone (profiling): the batched paged attention workload")
+    p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="write profiles/traffic.json from two rocprofv3 --pmc runs of --counters and exit")
     return p.parse_args()
 
 
@@ -57,9 +61,36 @@ def flush_caches():
     _FLUSH.sum()
 
 
-def alternating_ms(fns, replays=5):
-    """Average duration of one launch over back-to-back launches of fns[0], fns[1], ... captured
-    in a HIP graph and replayed, timed with one pair of HIP events on the current stream."""
+def stats(xs):
+    """mean, median, p10, p90 (and the count) of a list of durations."""
+    a = np.asarray(xs, dtype=np.float64)
+    return {"mean": float(a.mean()), "median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "n": int(a.size)}
+
+
+def rounded(st, nd=5):
+    return {k: (round(v, nd) if isinstance(v, float) else v) for k, v in st.items()}
+
+
+def replay_times_ms(g, n, flush=False):
+    """Duration of each of n replays of graph g, one HIP event pair per replay on the current stream
+    (the stream the library launches on)."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for s_, e_ in evs:
+        if flush:
+            flush_caches()
+        s_.record()
+        g.replay()
+        e_.record()
+    torch.cuda.synchronize()
+    return [s_.elapsed_time(e_) for s_, e_ in evs]
+
+
+def alternating_ms(fns, replays=50, flush=False):
+    """Per-launch duration statistics of back-to-back launches of fns[0], fns[1], ... captured in a
+    HIP graph: each replay is timed with its own HIP event pair and divided by the launches it
+    holds.  ``flush`` evicts the caches before every replay (a cold start per replay)."""
     import torch
     for f in fns:
         f()
@@ -71,24 +102,19 @@ def alternating_ms(fns, replays=5):
     g.replay()
     torch.cuda.synchronize()
     flush_caches()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    for _ in range(replays):
-        g.replay()
-    e.record()
-    torch.cuda.synchronize()
+    per = [t / len(fns) for t in replay_times_ms(g, replays, flush)]
     del g
-    return s.elapsed_time(e) / (replays * len(fns))
+    return stats(per)
 
 
-def layer_sweep_ms(fn, n_layers, sweeps=4):
-    """Average duration of one launch of `fn(layer)` over back-to-back launches that walk every
-    layer's weights and caches in turn (as the round does).  The layers' operands together exceed
-    the 256 MiB infinity cache, so each launch streams its own from HBM."""
+def layer_sweep_ms(fn, n_layers, sweeps=50):
+    """Per-launch statistics of `fn(layer)` over back-to-back launches that walk every layer's
+    weights and caches in turn (as the round does).  The layers' operands together exceed the
+    256 MiB infinity cache, so each launch streams its own from HBM."""
     return alternating_ms([(lambda i=i: fn(i)) for i in range(n_layers)], sweeps)
 
 
-def kernel_table(dec, ctx_np):
+def kernel_table(dec, ctx_np, sweeps=50):
     """Per-launch HIP-event times of each kernel class of the round at its in-round shapes."""
     import orthrus_round_amd._lib as L
     s, B, K = dec.shape, dec.B, dec.K
@@ -104,8 +130,8 @@ def kernel_table(dec, ctx_np):
     tab = {}
 
     def add(name, fn, per_round, bytes_, flops):
-        ms = layer_sweep_ms(fn, nl)
-        tab[name] = dict(ms=ms, per_round=per_round, bytes=bytes_, flops=flops)
+        st = layer_sweep_ms(fn, nl, sweeps)
+        tab[name] = dict(ms=st["mean"], stats=st, per_round=per_round, bytes=bytes_, flops=flops)
 
     add("gemm_qkv_rope_kv", lambda i: L.gemm_rope_kv_write(B, K, Hq, Hkv, D, dec.page, dec.max_pages, H, dt, dec.a,
                                                           Ly[i]["qkv_ar"], dec.rope, dec.max_pos, dec.ctx_len, None,
@@ -185,7 +211,7 @@ def roofline_of(name, rec, bound="hbm"):
             "ms_per_launch": round(rec["ms"], 5)}
 
 
-def attention_roofline(kv_chunk):
+def attention_roofline(kv_chunk, replays=50):
     """Draft + verify attention at batch 16, 32Q/8KV heads, D 128, ragged contexts 512..16384,
     16-token pages in a seeded random order (bf16 in, fp32 out).  Launches alternate between two
     copies of the paged cache (449 MB each, together 3.5x the 256 MiB infinity cache), so every
@@ -208,14 +234,19 @@ def attention_roofline(kv_chunk):
     out = torch.empty((16, 32, 32, 128), dtype=torch.float32, device="cuda")
     res = {}
     n_sum = int(ctx.sum())
-    for name, mk, keys in [
-        ("draft", lambda pk, pv: (lambda: ora.draft_attn(desc, q, pk, pv, pt, cl, kb, vb, out, ws)), n_sum + 16 * 32),
-        ("verify", lambda pk, pv: (lambda: ora.verify_attn(desc, q, pk, pv, pt, cl, out, ws)), n_sum + 16 * 32),
+    for name, mk in [
+        ("draft", lambda pk, pv: (lambda: ora.draft_attn(desc, q, pk, pv, pt, cl, kb, vb, out, ws))),
+        ("verify", lambda pk, pv: (lambda: ora.verify_attn(desc, q, pk, pv, pt, cl, out, ws))),
     ]:
+        # K and V of every cached key (plus the draft's block keys), the queries and the output
+        keys = n_sum + (16 * 32 if name == "draft" else 0)
         byts = keys * 8 * 128 * 2 * 2 + q.numel() * 2 + out.numel() * 4
-        ms = alternating_ms([mk(pk, pv) for pk, pv in pages])
-        res[name] = {"ms": round(ms, 5), "bytes": byts, "GBs": round(byts / ms / 1e6, 1),
-                     "frac": round(byts / ms / 1e6 / HBM_PEAK_GBS, 4)}
+        st = alternating_ms([mk(pk, pv) for pk, pv in pages], replays)
+        flops = 4 * 32 * 128 * 32 * (n_sum + 16 * 32)
+        res[name] = {"ms": round(st["mean"], 5), "ms_stats": rounded(st), "bytes": byts,
+                     "GBs": round(byts / st["mean"] / 1e6, 1), "frac": round(byts / st["mean"] / 1e6 / HBM_PEAK_GBS, 4),
+                     "frac_median": round(byts / st["median"] / 1e6 / HBM_PEAK_GBS, 4),
+                     "mfma_frac": round(flops / st["mean"] / 1e9 / BF16_PEAK_TFLOPS, 4)}
     del pages
     torch.cuda.empty_cache()
     return {"workload": "batch 16, 32Q/8KV, D128, ctx U[512,16384], 16-token paged random order, bf16->fp32, "
@@ -224,45 +255,192 @@ def attention_roofline(kv_chunk):
             "sum_ctx": n_sum, "kv_chunk": kv_chunk, **res}
 
 
-def cpu_baseline(W, shape, prompts_np, tokens_per_round_seq, kv_seed=9):
-    """The CPU oracle (float64, batched BLAS rows) on a bounded sample: one draft + verify
-    round of ONE sequence through layer 0 of the 8 (plus the LM head), over a synthetic
-    4095-token AR cache; scaled to the whole model as layers x (layer time) + LM head."""
-    import dataclasses
+def attention_c2(replays=50):
+    """One attention layer at Qwen3-1.7B shape (batch 1, 16Q/8KV heads x 128, bf16 in, fp32 out,
+    32 block queries, both masks) at cache lengths 1024, 4096 and 8192.  Each call is timed cold:
+    the caches are evicted by a 512 MiB read before it.  These calls move 4.7 to 34 MB, below
+    launch scale (one workgroup per kv head and key chunk)."""
+    import torch
+    import orthrus_round_amd as ora
+    import synth
+    res = {}
+    for n in (1024, 4096, 8192):
+        inp = synth.attn_inputs(2, np.array([n]), 16, 8, 128)
+        dv = lambda x, bf=True: (torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16) if bf
+                                 else torch.from_numpy(np.ascontiguousarray(x))).cuda()
+        maxp = inp.page_table.shape[1]
+        out = torch.empty((1, 32, 16, 128), dtype=torch.float32, device="cuda")
+        q, pk, pv = dv(inp.q), dv(np.nan_to_num(inp.pages_k)), dv(np.nan_to_num(inp.pages_v))
+        pt, cl, kb, vb = dv(inp.page_table, False), dv(inp.ctx, False), dv(inp.k_blk), dv(inp.v_blk)
+        row = {}
+        for chunk in (0, 512):
+            desc = ora.attn_desc(1, 16, 8, 128, 32, 16, maxp, maxp * 16, chunk, ora.BF16, ora.F32, 1.0)
+            ws = torch.empty(max(16, ora.attn_workspace_bytes(desc)), dtype=torch.uint8, device="cuda")
+            for name in ("draft", "verify"):
+                fn = ((lambda: ora.draft_attn(desc, q, pk, pv, pt, cl, kb, vb, out, ws)) if name == "draft" else
+                      (lambda: ora.verify_attn(desc, q, pk, pv, pt, cl, out, ws)))
+                st = alternating_ms([fn], replays, flush=True)
+                byts = 4096 * n + (128 * 1024 if name == "draft" else 4096 * 32) + 128 * 1024 + 256 * 1024
+                flops = 4 * 16 * 128 * 32 * (n + 32)
+                row[f"{name}_chunk{chunk or 1024}"] = {
+                    "ms_stats": rounded(st, 6), "bytes": byts, "GBs_median": round(byts / st["median"] / 1e6, 1),
+                    "frac_median": round(byts / st["median"] / 1e6 / HBM_PEAK_GBS, 4),
+                    "mfma_frac_median": round(flops / st["median"] / 1e9 / BF16_PEAK_TFLOPS, 5)}
+        res[str(n)] = row
+    return {"workload": "batch 1, 16Q/8KV x 128, 32 block queries, bf16 -> fp32, cold (caches evicted before "
+                        "every call); kv_chunk 1024 (one chunk up to 1K keys) and 512 (more workgroups)", **res}
+
+
+def lmhead_consensus_c4(replays=50):
+    """LM head + consensus at the 8B shape: h [16*32, 4096] bf16 ~ N(0,1), W [151936, 4096] bf16 ~
+    N(0, 0.02); the LM head (greedy argmax) as a fraction of the bf16 MFMA peak and of HBM; the
+    greedy consensus/commit and the T = 0.8 rejection accept (draft hidden 0.9 h + sqrt(0.19) N(0,1)
+    through the same head) as latency per call."""
+    import torch
+    import orthrus_round_amd as ora
+    import synth
+    B, K, H, V, T = 16, 32, 4096, 151936, 0.8
+    M = B * K
+    ht, w = synth.lmhead_inputs(4, M, H, V)
+    hd = synth.draft_hidden(4, ht, mix=0.9)
+    dv = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).cuda()
+    h_t, hd_t, w_t = dv(ht), dv(hd), dv(w)
+    seqs = torch.arange(B, dtype=torch.int32, device="cuda")
+    rnds = torch.zeros(B, dtype=torch.int32, device="cuda")
+    d0 = ora.lmhead_desc(M, H, V, ora.BF16, K)
+    ws = torch.empty(ora.lmhead_workspace_bytes(d0), dtype=torch.uint8, device="cuda")
+    tok = torch.empty(M, dtype=torch.int32, device="cuda")
+    st_lm = alternating_ms([lambda: ora.lmhead_argmax(d0, h_t, w_t, seqs, rnds, tok, None, None, ws)], replays)
+    flops, byts = 2 * M * V * H, (V * H + M * H) * 2
+    res = {"lmhead_argmax_m512": {"ms_stats": rounded(st_lm), "flops": flops, "bytes": byts,
+                                  "TFLOPs_median": round(flops / st_lm["median"] / 1e9, 1),
+                                  "mfma_frac_median": round(flops / st_lm["median"] / 1e9 / BF16_PEAK_TFLOPS, 4),
+                                  "hbm_frac_median": round(byts / st_lm["median"] / 1e6 / HBM_PEAK_GBS, 4)}}
+    # drafts: the target argmax for a geometric prefix, then random (accept = the prefix length)
+    ora.lmhead_argmax(d0, h_t, w_t, seqs, rnds, tok, None, None, ws)
+    t_np = tok.cpu().numpy().reshape(B, K)
+    d_np, L = synth.geometric_drafts(4, t_np, V)
+    d_t, t_t = torch.from_numpy(d_np).cuda(), torch.from_numpy(t_np).cuda()
+    state = {k: torch.zeros(B, dtype=torch.int32, device="cuda") for k in ("anchor", "accept", "out_len", "round")}
+    done = torch.zeros(B, dtype=torch.int32, device="cuda")
+    ctx = torch.full((B,), 1000, dtype=torch.int32, device="cuda")
+    outb = torch.full((B, 64), -1, dtype=torch.int32, device="cuda")
+
+    def reset():
+        state["out_len"].zero_()
+        ctx.fill_(1000)
+
+    def commit():
+        reset()
+        ora.consensus_commit(B, K, d_t, t_t, ctx, state["anchor"], state["accept"], outb, state["out_len"],
+                             state["round"], done, 64, 1 << 30)
+    st_c = alternating_ms([commit], replays)
+    commit()
+    torch.cuda.synchronize()
+    res["consensus_commit_b16"] = {"us_stats": rounded({k: (v * 1e3 if k != "n" else v) for k, v in st_c.items()}, 2),
+                                   "accepts_equal_prefix": bool(np.array_equal(state["accept"].cpu().numpy(), L)),
+                                   "note": "includes a reset of two [16] state tensors (two small fill kernels)"}
+    # T = 0.8: draft logits + lse (sampled call), target logits + lse (argmax call), then the accept
+    zd = torch.empty((M, V), dtype=torch.float32, device="cuda")
+    zt = torch.empty_like(zd)
+    ld, lt = torch.empty(M, dtype=torch.float32, device="cuda"), torch.empty(M, dtype=torch.float32, device="cuda")
+    dd = ora.lmhead_desc(M, H, V, ora.BF16, K, ora.STREAM_DRAFT, T, 77)
+    dt_ = ora.lmhead_desc(M, H, V, ora.BF16, K, ora.STREAM_AR, T, 77, sample=False)
+    dtok = torch.empty(M, dtype=torch.int32, device="cuda")
+    st_ls = alternating_ms([lambda: ora.lmhead_argmax(dd, hd_t, w_t, seqs, rnds, dtok, zd, ld, ws)], 10)
+    ora.lmhead_argmax(dt_, h_t, w_t, seqs, rnds, tok, zt, lt, ws)
+
+    def rej():
+        reset()
+        ora.rejection_accept(B, K, V, T, 77, seqs, zd, zt, ld, lt, dtok, ctx, state["anchor"], state["accept"], outb,
+                             state["out_len"], rnds, done, 64, 1 << 30)
+    st_r = alternating_ms([rej], replays)
+    res["lmhead_sampled_with_logits_m512"] = {"ms_stats": rounded(st_ls),
+                                              "note": "Gumbel-max sample + fp32 logits (311 MB) + logsumexp"}
+    res["rejection_accept_b16_t0.8"] = {"us_stats": rounded({k: (v * 1e3 if k != "n" else v) for k, v in st_r.items()}, 2),
+                                        "accepts": [int(x) for x in state["accept"].cpu().numpy()],
+                                        "note": "includes the same state reset as the consensus timing"}
+    del zd, zt, w_t
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(W, shape, prompts_np, kv_seed=9):
+    """The CPU oracle as it stands (float64 NumPy, BLAS over rows) on a bounded sample of the timed
+    workload: one whole draft + verify + consensus round of ONE sequence through all layers and the
+    LM head, over a synthetic AR cache of prompt-1 keys per layer (prefill excluded); reported as
+    that round's committed tokens per second.  Beside it, one call of the attention-only workloads
+    and a 32-row slice of the LM-head workload, each on its own seeded inputs."""
     from oracle import decode as Dc
     from oracle import model as M
     import synth
-    one = dataclasses.replace(shape, layers=1)
-    keys = ["embed", "lm_head", "final_norm"] + [k for k in W if k.startswith("0.")]
-    Wt = M.Weights({k: W[k] for k in keys}, one)
+    nthreads = len(os.sched_getaffinity(0))
+    t_conv = time.perf_counter()
+    Wt = M.Weights(W, shape)
+    t_conv = time.perf_counter() - t_conv
     P = prompts_np.shape[1]
-    cache = Dc.Cache(one, P + 64, np.float64)
+    cache = Dc.Cache(shape, P + 64, np.float64)
     rs = np.random.default_rng(kv_seed)
-    cache.k[0][: P - 1] = rs.standard_normal((P - 1, one.kv_heads, one.head_dim))
-    cache.v[0][: P - 1] = rs.standard_normal((P - 1, one.kv_heads, one.head_dim))
+    for l in range(shape.layers):
+        cache.k[l][: P - 1] = rs.standard_normal((P - 1, shape.kv_heads, shape.head_dim))
+        cache.v[l][: P - 1] = rs.standard_normal((P - 1, shape.kv_heads, shape.head_dim))
     cache.n = P - 1
     anchor = int(prompts_np[0, -1])
-    nthreads = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
-    zd = Dc.draft_pass(Wt, cache, [anchor] + [one.mask_id] * 31, rowwise=False)
-    t1 = time.perf_counter()
-    zt = Dc.ar_pass(Wt, cache, [anchor] + list(M.argmax_lowest(zd)[:31]), rowwise=False)
-    t2 = time.perf_counter()
-    # LM head share: time it alone to separate it from the layer
-    h = np.ones((32, one.hidden))
-    t3 = time.perf_counter()
-    M.lm_logits(Wt, h, rowwise=False)
-    t4 = time.perf_counter()
-    lm = t4 - t3
-    layer = (t2 - t0) - 2 * lm
-    full_round = shape.layers * layer + 2 * lm
-    value = tokens_per_round_seq / full_round
-    return {"value": round(value, 4), "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
-            "sample": (f"float64 NumPy oracle, one round (draft+verify) of 1 sequence through layer 0 plus the LM "
-                       f"head over a synthetic {P - 1}-token cache; measured {t2 - t0:.2f}s, scaled to "
-                       f"{shape.layers} layers = {full_round:.2f}s per round at the GPU's "
-                       f"{tokens_per_round_seq:.3f} committed tokens per round per sequence"),
-            "round_s": round(full_round, 3)}
+    zd = Dc.draft_pass(Wt, cache, [anchor] + [shape.mask_id] * 31, rowwise=False)
+    d = M.argmax_lowest(zd)
+    zt = Dc.ar_pass(Wt, cache, [anchor] + [int(x) for x in d[:31]], rowwise=False)
+    k, emitted = Dc.consensus(d, M.argmax_lowest(zt))
+    round_s = time.perf_counter() - t0
+    del Wt, cache
+    per = {}
+    # one attention call of the single-layer workload (n = 8192, draft mask), row-by-row oracle
+    inp = synth.attn_inputs(2, np.array([8192]), 16, 8, 128)
+    ta = time.perf_counter()
+    k_, v_ = inp.kv[0]
+    M.draft_attention(inp.q[0].astype(np.float64), k_[:8192].astype(np.float64), v_[:8192].astype(np.float64),
+                      inp.k_blk[0].astype(np.float64), inp.v_blk[0].astype(np.float64), 1.0)
+    per["attn_qwen3_1p7b_n8192_draft"] = {"s": round(time.perf_counter() - ta, 3), "sample": "one whole call"}
+    # one call of the batched paged workload (draft mask), matrix-product form of the oracle
+    ctx = synth.ragged_lengths(3, 16, 512, 16384)
+    inp = synth.attn_inputs(3, ctx, 32, 8, 128)
+    ta = time.perf_counter()
+    for b in range(16):
+        n = int(ctx[b])
+        k_, v_ = inp.kv[b]
+        M.grouped_attention(inp.q[b].astype(np.float64),
+                            np.concatenate([k_[:n], inp.k_blk[b]]).astype(np.float64),
+                            np.concatenate([v_[:n], inp.v_blk[b]]).astype(np.float64),
+                            np.ones((32, n + 32), bool), 1.0)
+    per["attn_qwen3_8b_batch16_draft"] = {"s": round(time.perf_counter() - ta, 3), "sample": "one whole call"}
+    del inp
+    # the LM head of one sequence's 32 rows of the 512-row workload, plus its consensus
+    h, w = synth.lmhead_inputs(4, 32, 4096, 151936)
+    ta = time.perf_counter()
+    z = h.astype(np.float64) @ w.astype(np.float64).T
+    t = M.argmax_lowest(z)
+    Dc.consensus(t, t)
+    lm_s = time.perf_counter() - ta
+    per["lmhead_consensus_8b_32_of_512_rows"] = {"s": round(lm_s, 3), "whole_call_s_scaled": round(16 * lm_s, 3),
+                                                 "sample": "32 of the 512 rows (float64 product incl. conversion)"}
+    return {"value": round(len(emitted) / round_s, 4), "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": (f"float64 NumPy oracle, one whole round (draft pass, verify pass, consensus) of 1 sequence "
+                       f"through all {shape.layers} layers and the LM head over a synthetic {P - 1}-token cache per "
+                       f"layer (prefill excluded): {round_s:.2f}s, {len(emitted)} token(s) committed (accept {k}); "
+                       f"weights cast to float64 beforehand in {t_conv:.1f}s"),
+            "round_s": round(round_s, 3), "per_config": per}
 
 
 def calibration_copy():
@@ -276,8 +454,10 @@ def calibration_copy():
     del cal_src, cal_dst
 
 
-def block_sweep(dec, prompts, blocks=(4, 8, 16, 32), rounds=12):
-    """Round latency (graph replay, ms) of the same model and context for each block size."""
+def block_sweep(dec, prompts, blocks=(4, 8, 16, 32), rounds=30):
+    """Round latency (graph replay, per-round HIP events) of the same model and context for each
+    block size, the round's HBM roofline fraction at that size, and the per-launch time of each
+    kernel class at that size (the GEMMs' M is batch x block)."""
     import torch
     res = {}
     for K in blocks:
@@ -287,14 +467,55 @@ def block_sweep(dec, prompts, blocks=(4, 8, 16, 32), rounds=12):
         for _ in range(2):
             g.replay()
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(rounds):
-            g.replay()
-        torch.cuda.synchronize()
-        res[str(K)] = round((time.perf_counter() - t0) / rounds * 1e3, 4)
+        st = stats(replay_times_ms(g, rounds))
         del g
+        ctx_np = dec.ctx_len.cpu().numpy()
+        tab = kernel_table(dec, ctx_np, sweeps=12)
+        byts = round_bytes(dec, ctx_np)
+        res[str(K)] = {"round_ms": rounded(st, 4), "round_bytes": byts,
+                       "round_hbm_frac_median": round(byts / st["median"] / 1e6 / HBM_PEAK_GBS, 4),
+                       "kernels_ms": {k: round(v["stats"]["median"], 5) for k, v in tab.items()},
+                       "kernels_ms_per_round": {k: round(v["stats"]["median"] * v["per_round"], 4)
+                                                for k, v in tab.items()}}
     dec.set_block(dec.block_alloc)
     return res
+
+
+def round_bytes(dec, ctx_np):
+    """Algorithmic HBM bytes of one greedy round: both views' layer weights (each pass streams its
+    view's attention weights and the shared MLP), the LM head twice, every cached key's K and V per
+    layer per pass, and the activations in and out of each kernel are neglected (< 1%)."""
+    s = dec.shape
+    esz = 2 if dec.prec == "bf16" else 4
+    H, D, Hq, Hkv, I, V = s.hidden, s.head_dim, s.q_heads, s.kv_heads, s.inter, s.vocab
+    attn_w = (Hq + 2 * Hkv) * D * H + H * Hq * D
+    layer_w = attn_w + 3 * I * H
+    kv = int(ctx_np.sum()) * Hkv * D * 2
+    return 2 * (s.layers * (layer_w + kv) + V * H) * esz
+
+
+def sampled_round(dec, prompts, temperature=0.8, seed=11, rounds=30):
+    """The sampled round (T > 0): Gumbel-max drafts with logits and logsumexp kept, the verify pass
+    as an argmax call that keeps logits and lse(z/T), and the rejection accept; graph replay with
+    per-round HIP events, committed tokens per second over the timed rounds."""
+    import torch
+    B = len(prompts)
+    dec.prefill(torch.from_numpy(prompts), max_out=32 * (rounds + 4))
+    g = dec.capture(dec.round_sampled, temperature, seed)
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    out0 = int(dec.out_len.sum())
+    t0 = time.perf_counter()
+    for _ in range(rounds):
+        g.replay()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    committed = int(dec.out_len.sum()) - out0
+    st = stats(replay_times_ms(g, rounds))
+    del g
+    return {"temperature": temperature, "round_ms": round(el / rounds * 1e3, 4), "round_ms_stats": rounded(st, 4),
+            "tokens_per_s": round(committed / el, 2), "tokens_per_round_per_seq": round(committed / (rounds * B), 4)}
 
 
 def two_step_drafting(dec, prompts, n_fill=15, rounds=12, n_tokens=32):
@@ -437,8 +658,125 @@ def memory_overhead(W, shape, batch, kv_chunk, contexts=(1024, 2048, 4096), roun
                     "and grows with the context"}
 
 
+def counter_marker():
+    """One tiny Philox dispatch that marks the start of the timed work in a counter run: the
+    summary keeps only the dispatches after it (so the prefill's chunks are not mixed in)."""
+    import torch
+    import orthrus_round_amd as ora
+    ctr = torch.zeros((1, 4), dtype=torch.int64, device="cuda")
+    out = torch.empty((1, 4), dtype=torch.int64, device="cuda")
+    ora.philox4x64(1, ctr, 0, 0, out)
+    torch.cuda.synchronize()
+
+
+MARKER_KERNEL = "philox_kernel"
+CALIBRATION_KERNEL = "copyBuffer"
+
+
+def summarize_counters(fetch_dir, write_dir, out_json):
+    """Build profiles/traffic.json from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of
+    `bench.py --counters`: per bench kernel, the median KiB per dispatch over the dispatches after
+    the marker, scaled by what the same counter read for the 256 MiB calibration copy."""
+    import csv
+    import glob
+
+    def load(d, counter):
+        rows = []
+        for path in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    if r["Counter_Name"] == counter:
+                        rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+        rows.sort()
+        start = next(i for i, (_, k, _) in enumerate(rows) if MARKER_KERNEL in k)
+        return rows[start + 1:]
+
+    fetch, write = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+    cal_f = [v for _, k, v in fetch if CALIBRATION_KERNEL in k]
+    cal_w = [v for _, k, v in write if CALIBRATION_KERNEL in k]
+    f_scale, w_scale = 262144.0 / cal_f[-1], 262144.0 / cal_w[-1]
+    # which dispatched kernels make up each bench kernel (name fragments, in call order)
+    parts = {
+        "gemm_qkv_rope_kv": ["gemm_quarter_kernel", "gemm_reduce_rope_kv_kernel"],
+        "gemm_o_residual_rmsnorm": ["gemm_quarter_kernel", "gemm_reduce_rmsnorm_kernel"],
+        "gemm_gate_up_swiglu": ["gemm_kernel"],
+        "gemm_down_residual_rmsnorm": ["gemm_quarter_kernel", "gemm_reduce_rmsnorm_kernel"],
+        "attn_draft": ["attn_kernel", "attn_combine_kernel"],
+        "attn_verify": ["attn_kernel", "attn_combine_kernel"],
+        "lmhead_argmax": ["lmhead_kernel", "lmhead_kernel", "lmhead_finalize"],
+    }
+    # the round's dispatch sequence per pass and layer, as the decoder enqueues it
+    seq_f = [(k, v) for _, k, v in fetch if CALIBRATION_KERNEL not in k]
+    seq_w = [(k, v) for _, k, v in write if CALIBRATION_KERNEL not in k]
+    per = {name: {"fetch": [], "write": [], "kernels": set()} for name in parts}
+
+    def walk(seq, key):
+        i = 0
+        order = []
+        while i < len(seq):
+            k = seq[i][0]
+            if "embed_kernel" in k or "rmsnorm_kernel" in k and "gemm" not in k or "consensus" in k:
+                i += 1
+                continue
+            if "gemm_quarter_kernel" in k and i + 1 < len(seq):
+                nxt = seq[i + 1][0]
+                if "rope_kv" in nxt:
+                    name = "gemm_qkv_rope_kv"
+                elif "attn_kernel" in (seq[i - 1][0] if i else "") or "attn_combine" in (seq[i - 1][0] if i else ""):
+                    name = "gemm_o_residual_rmsnorm"
+                else:
+                    name = "gemm_down_residual_rmsnorm"
+                order.append((name, [seq[i], seq[i + 1]]))
+                i += 2
+            elif "gemm_kernel" in k:
+                order.append(("gemm_gate_up_swiglu", [seq[i]]))
+                i += 1
+            elif "attn_kernel" in k:
+                draft = "Lb1E" in k or ", true>" in k
+                grp = [seq[i]]
+                if i + 1 < len(seq) and "attn_combine" in seq[i + 1][0]:
+                    grp.append(seq[i + 1])
+                    i += 1
+                order.append(("attn_draft" if draft else "attn_verify", grp))
+                i += 1
+            elif "lmhead_kernel" in k:
+                grp = [seq[i]]
+                while i + 1 < len(seq) and ("lmhead_kernel" in seq[i + 1][0] or "lmhead_finalize" in seq[i + 1][0]):
+                    grp.append(seq[i + 1])
+                    i += 1
+                order.append(("lmhead_argmax", grp))
+                i += 1
+            else:
+                i += 1
+        for name, grp in order:
+            per[name][key].append(sum(v for _, v in grp))
+            per[name]["kernels"].update(k for k, _ in grp)
+
+    walk(seq_f, "fetch")
+    walk(seq_w, "write")
+    out = {"fetch_scale": f_scale, "write_scale": w_scale, "bench_kernels": {}}
+    for name, rec in per.items():
+        if not rec["fetch"] or not rec["write"]:
+            continue
+        fk, wk = float(np.median(rec["fetch"])), float(np.median(rec["write"]))
+        out["bench_kernels"][name] = {
+            "rocprof_kernels": sorted(rec["kernels"]), "dispatch_groups": len(rec["fetch"]),
+            "fetch_kib": fk, "write_kib": wk, "bytes": int(round((fk * f_scale + wk * w_scale) * 1024)),
+            "source_sha256": source_digest(name)}
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=1)
+    return out
+
+
 def main():
     args = parse()
+    if args.summarize_counters:
+        fd, wd = args.summarize_counters
+        out = summarize_counters(fd, wd, os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                                                      "traffic.json"))
+        print(json.dumps({k: {"bytes": v["bytes"], "groups": v["dispatch_groups"]}
+                          for k, v in out["bench_kernels"].items()}))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode round is sharded by "
               "sequence across GPUs with no exchange, so N GPUs = N independent copies of this run.")
@@ -448,6 +786,15 @@ def main():
     from orthrus_round_amd.decoder import Decoder
     import orthrus_round_amd as ora
     ora.lib()
+    if args.only == "attn-c3":
+        # the batched paged attention workload alone (profiling runs)
+        if args.counters:
+            counter_marker()
+        attn = attention_roofline(args.attn_chunk, replays=args.steps)
+        calibration_copy()
+        print(json.dumps({"mode": "attn-c3", "attention_roofline": attn}), flush=True)
+        torch.cuda.synchronize()
+        return
     t_setup = time.perf_counter()
     shape = synth.QWEN3_8B_L8
     if args.layers != shape.layers:
@@ -457,14 +804,16 @@ def main():
     prompts = synth.prompt_ids(shape, 5, args.batch, args.prompt)
     total_rounds = args.warmup + args.steps + 2
     dec = Decoder(W, shape, precision=args.precision, block=32, max_batch=args.batch,
-                  max_ctx=args.prompt + 32 * total_rounds + 64, kv_chunk=args.kv_chunk)
+                  max_ctx=args.prompt + 32 * max(total_rounds, 70) + 64, kv_chunk=args.kv_chunk)
     print(f"[bench] setup {time.perf_counter() - t_setup:.1f}s", file=sys.stderr, flush=True)
-    dec.prefill(torch.from_numpy(prompts), max_out=32 * total_rounds)
+    dec.prefill(torch.from_numpy(prompts), max_out=32 * max(total_rounds, 70))
     torch.cuda.synchronize()
     g = dec.capture(dec.round_greedy)  # its warm-up call is one untimed round
     for _ in range(args.warmup):
         g.replay()
     torch.cuda.synchronize()
+    if args.counters:
+        counter_marker()
     out0 = int(dec.out_len.sum())
     r0 = dec.round.cpu().numpy().copy()
     t0 = time.perf_counter()
@@ -482,12 +831,26 @@ def main():
         calibration_copy()
         print(json.dumps({"mode": "counters", "rounds": args.steps, "ms_per_step": round(elapsed / args.steps * 1e3, 4)}),
               flush=True)
+        # leave nothing for interpreter teardown: the captured graph and the decoder's device
+        # buffers are released here, in order, while the runtime and any profiler tool are alive
+        del g
+        torch.cuda.synchronize()
+        del dec
+        torch.cuda.empty_cache()
         return
+    # per-round latency distribution (more replays than the timed steps when those are few)
+    n_stat = max(50, args.steps)
+    round_st = stats(replay_times_ms(g, n_stat))
+    del g
+    print("[bench] round distribution done", file=sys.stderr, flush=True)
     tab = kernel_table(dec, ctx_np)
     per_round = {k: v["ms"] * v["per_round"] for k, v in tab.items()}
     dominant = max(per_round, key=per_round.get)
     roof = roofline_of(dominant, tab[dominant], "mfma" if dominant == "lmhead_argmax" and args.batch * 32 >= 512
                        else "hbm")
+    roof["ms_stats"] = rounded(tab[dominant]["stats"])
+    rbytes = round_bytes(dec, ctx_np)
+    print("[bench] kernel table done", file=sys.stderr, flush=True)
 
     # AR yardstick on the same kernels (one causal row per sequence per step)
     dec.prefill(torch.from_numpy(prompts), max_out=64)
@@ -495,27 +858,40 @@ def main():
     for _ in range(3):
         ga.replay()
     torch.cuda.synchronize()
-    ta = time.perf_counter()
-    for _ in range(20):
-        ga.replay()
-    torch.cuda.synchronize()
-    ar_ms = (time.perf_counter() - ta) / 20 * 1e3
+    ar_st = stats(replay_times_ms(ga, 50))
+    ar_ms = ar_st["mean"]
+    del ga
 
-    sweep = match = control = memory = two = None
+    sampled = sweep = match = control = memory = two = c2 = c4 = None
     if not args.no_extras:
+        sampled = sampled_round(dec, prompts)
+        print("[bench] sampled round done", file=sys.stderr, flush=True)
         sweep = block_sweep(dec, prompts)
+        print("[bench] block sweep done", file=sys.stderr, flush=True)
         two = two_step_drafting(dec, prompts)
         match = trajectory_match(dec, W, shape, prompts, args.match_tokens, args.kv_chunk)
         control = divergence_control(dec, prompts, args.match_tokens, args.kv_chunk, args.control_chunk)
+        print("[bench] trajectories done", file=sys.stderr, flush=True)
         memory = memory_overhead(W, shape, args.batch, args.kv_chunk)
+    del dec
+    torch.cuda.empty_cache()
+    if not args.no_extras:
+        c2 = attention_c2()
+        c4 = lmhead_consensus_c4()
+        print("[bench] c2 / c4 legs done", file=sys.stderr, flush=True)
     attn = None if args.no_attn else attention_roofline(args.attn_chunk)
+    copy_gbs = stream_copy_gbs()
     calibration_copy()
+    torch.cuda.synchronize()
     tokens_per_round_seq = committed / (args.steps * args.batch)
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(W, shape, prompts, tokens_per_round_seq)
+        cpu = cpu_baseline(W, shape, prompts)
+        print("[bench] cpu baseline done", file=sys.stderr, flush=True)
 
     ms = elapsed / args.steps * 1e3
+    roof["copy_GBs"] = copy_gbs
+    roof["frac_of_copy"] = round(roof["achieved"] / copy_gbs, 4) if roof["unit"] == "GB/s" else None
     rec = {
         "metric": "accepted tokens/s (Orthrus decode rounds, committed tokens)",
         "value": round(committed / elapsed, 2),
@@ -534,16 +910,27 @@ def main():
                    "heads": f"{shape.q_heads}Q/{shape.kv_heads}KV x {shape.head_dim}", "inter": shape.inter,
                    "vocab": shape.vocab, "kv_chunk": args.kv_chunk, "parallelism": "single GPU"},
         "round_latency_ms": round(ms, 4),
+        "round_latency_stats_ms": rounded(round_st, 4),
+        "round_bytes": rbytes,
+        "round_hbm_frac_median": round(rbytes / round_st["median"] / 1e6 / HBM_PEAK_GBS, 4),
         "tokens_per_round_per_seq": round(tokens_per_round_seq, 4),
         "tpf": round(tokens_per_round_seq / 2, 4),
         "rounds_timed_min": rounds_done,
         "ar_step_ms": round(ar_ms, 4),
+        "ar_step_stats_ms": rounded(ar_st, 4),
         "ar_tokens_per_s": round(args.batch / ar_ms * 1e3, 2),
         "projected_tokens_per_s_at_pages_10p78_tokens_per_round": round(args.batch * 10.78 / ms * 1e3, 1),
         "roofline": roof,
-        "kernels": {k: {"ms": round(v["ms"], 5), "per_round": v["per_round"],
-                        "GBs": round(v["bytes"] / v["ms"] / 1e6, 1)} for k, v in tab.items()},
+        "stream_copy_GBs": copy_gbs,
+        "kernels": {k: {"ms": round(v["ms"], 5), "ms_median": round(v["stats"]["median"], 5),
+                        "ms_p10": round(v["stats"]["p10"], 5), "ms_p90": round(v["stats"]["p90"], 5),
+                        "per_round": v["per_round"], "GBs": round(v["bytes"] / v["ms"] / 1e6, 1),
+                        "hbm_frac": round(v["bytes"] / v["ms"] / 1e6 / HBM_PEAK_GBS, 4),
+                        "mfma_frac": round(v["flops"] / v["ms"] / 1e9 / BF16_PEAK_TFLOPS, 4)} for k, v in tab.items()},
+        "sampled_round": sampled,
         "attention_roofline": attn,
+        "attention_single_layer_qwen3_1p7b": c2,
+        "lmhead_consensus_8b": c4,
         "round_ms_by_block": sweep,
         "two_step_drafting": two,
         "trajectory_match_vs_ar": match,
@@ -552,6 +939,26 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+    torch.cuda.synchronize()
+
+
+def stream_copy_gbs(nbytes=1 << 30, reps=10):
+    """A plain device-to-device copy of 1 GiB (read + write counted), median over reps: the
+    practical HBM ceiling beside the published 8 TB/s."""
+    import torch
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    ts = []
+    for _ in range(reps):
+        s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_.record()
+        b.copy_(a)
+        e_.record()
+        torch.cuda.synchronize()
+        ts.append(s_.elapsed_time(e_))
+    del a, b
+    torch.cuda.empty_cache()
+    return round(2 * nbytes / float(np.median(ts)) / 1e6, 1)
 
 
 if __name__ == "__main__":
