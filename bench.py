@@ -38,11 +38,14 @@ def parse():
     p.add_argument("--no-extras", action="store_true", help="skip the block sweep and trajectory match")
     p.add_argument("--counters", action="store_true",
                    help="hardware-counter mode: prefill, the timed rounds and the calibration copy only")
+    p.add_argument("--block", type=int, default=32, help="rows per sequence of the timed rounds (block size K)")
     p.add_argument("--match-tokens", type=int, default=64)
     p.add_argument("--control-chunk", type=int, default=1024,
                    help="kv_chunk of the divergence control runs (another key summation order)")
     p.add_argument("--only", choices=["attn-c3"], default=None,
                    help="run one workload alone (profiling): the batched paged attention workload")
+    p.add_argument("--study", choices=["divergence"], default=None,
+                   help="run the stratified divergence study (64 sequences x 512 tokens) instead of the bench")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="write profiles/traffic.json from two rocprofv3 --pmc runs of --counters and exit")
     return p.parse_args()
@@ -620,6 +623,74 @@ def ar_margins(dec, prompts, n_tokens):
     return {"tokens": dec.out_tokens.cpu().numpy()[:B, :n_tokens], "top2_gap": gaps}
 
 
+def divergence_study(W, shape, n_seq=64, n_tokens=512, prompt_len=512, kv_chunk=640, other_chunk=1024):
+    """Trajectory match of greedy Orthrus against greedy AR, stratified by how decisive the AR model
+    is at each token (the gap between its two largest logits, in deciles over every reference token).
+
+    Pairs, each over n_seq sequences x n_tokens tokens:
+      * bf16 Orthrus vs bf16 AR and fp32 Orthrus vs fp32 AR, both through the same kernels at one
+        key chunking (every kernel's per-row result is independent of the batch and block, so these
+        are expected to match exactly);
+      * controls with another key summation order (kv_chunk other_chunk against kv_chunk), the
+        difference a kernel that is not batch-invariant makes between an Orthrus pass and an AR
+        step: bf16 AR vs bf16 AR, and bf16 Orthrus vs bf16 AR.
+    For a pair, a sequence contributes every token up to and including its first divergence; the
+    divergence rate of a decile is (first divergences in it) / (contributed tokens in it)."""
+    import torch
+    import synth
+    from orthrus_round_amd.decoder import Decoder
+    prompts = synth.prompt_ids(shape, 11, n_seq, prompt_len)
+    max_ctx = prompt_len + n_tokens + 96
+    runs = {}
+    say = lambda m: print(f"[study] {m}", file=sys.stderr, flush=True)
+    dec = Decoder(W, shape, precision="bf16", block=32, max_batch=n_seq, max_ctx=max_ctx, kv_chunk=kv_chunk)
+    runs["orthrus_bf16"], _ = dec.generate(prompts, n_tokens, use_graph=True, poll_every=32)
+    say("bf16 orthrus done")
+    runs["ar_bf16"], _ = dec.generate_ar(prompts, n_tokens, use_graph=True)
+    margins = ar_margins(dec, prompts, n_tokens)
+    assert np.array_equal(margins["tokens"], runs["ar_bf16"][:, :n_tokens]), "eager AR differs from the graph run"
+    say("bf16 ar and margins done")
+    dec.set_kv_chunk(other_chunk)
+    runs["ar_bf16_other_chunk"], _ = dec.generate_ar(prompts, n_tokens, use_graph=True)
+    del dec
+    torch.cuda.empty_cache()
+    d32 = Decoder(W, shape, precision="fp32", block=32, max_batch=n_seq, max_ctx=max_ctx, kv_chunk=kv_chunk)
+    runs["orthrus_fp32"], _ = d32.generate(prompts, n_tokens, use_graph=True, poll_every=32)
+    say("fp32 orthrus done")
+    runs["ar_fp32"], _ = d32.generate_ar(prompts, n_tokens, use_graph=True)
+    say("fp32 ar done")
+    del d32
+    torch.cuda.empty_cache()
+    gap = margins["top2_gap"]
+    edges = np.quantile(gap, np.linspace(0, 1, 11))
+    dec_of = np.clip(np.searchsorted(edges, gap, side="right") - 1, 0, 9)
+
+    def pair(x, y):
+        n_tok = np.zeros(10, np.int64)
+        n_div = np.zeros(10, np.int64)
+        firsts = []
+        for i in range(n_seq):
+            d = first_divergence(runs[x][i, :n_tokens], runs[y][i, :n_tokens])
+            upto = n_tokens if d is None else d + 1
+            np.add.at(n_tok, dec_of[i, :upto], 1)
+            if d is not None:
+                n_div[dec_of[i, d]] += 1
+                firsts.append(d)
+        return {"match_rate": round(1 - len(firsts) / n_seq, 4), "diverged": len(firsts),
+                "first_divergence_median": (float(np.median(firsts)) if firsts else None),
+                "by_margin_decile": [{"decile": q + 1, "gap_range": [round(float(edges[q]), 5), round(float(edges[q + 1]), 5)],
+                                      "tokens": int(n_tok[q]), "divergences": int(n_div[q]),
+                                      "rate": (round(float(n_div[q] / n_tok[q]), 6) if n_tok[q] else None)}
+                                     for q in range(10)]}
+    return {"sequences": n_seq, "tokens": n_tokens, "prompt_len": prompt_len, "kv_chunk": kv_chunk,
+            "control_kv_chunk": other_chunk,
+            "ar_top2_gap_quantiles": [round(float(e), 5) for e in edges],
+            "bf16_orthrus_vs_ar": pair("orthrus_bf16", "ar_bf16"),
+            "fp32_orthrus_vs_ar": pair("orthrus_fp32", "ar_fp32"),
+            "control_bf16_ar_vs_ar_other_chunk": pair("ar_bf16", "ar_bf16_other_chunk"),
+            "control_bf16_orthrus_vs_ar_other_chunk": pair("orthrus_bf16", "ar_bf16_other_chunk")}
+
+
 def memory_overhead(W, shape, batch, kv_chunk, contexts=(1024, 2048, 4096), rounds=4):
     """Device memory of an Orthrus decoder (32-row rounds) against an AR decoder (1-row steps) with
     caches sized for each context.  Every buffer is allocated up front, so holding a cache for a
@@ -786,6 +857,15 @@ def main():
     from orthrus_round_amd.decoder import Decoder
     import orthrus_round_amd as ora
     ora.lib()
+    if args.study == "divergence":
+        import synth
+        W = synth.model_weights(synth.QWEN3_8B_L8, cfg=5, diff_std=0.002, bf16=True)
+        t0 = time.perf_counter()
+        res = divergence_study(W, synth.QWEN3_8B_L8, kv_chunk=args.kv_chunk, other_chunk=args.control_chunk)
+        res["wall_s"] = round(time.perf_counter() - t0, 1)
+        print(json.dumps({"mode": "divergence-study", **res}), flush=True)
+        torch.cuda.synchronize()
+        return
     if args.only == "attn-c3":
         # the batched paged attention workload alone (profiling runs)
         if args.counters:
@@ -806,6 +886,8 @@ def main():
     dec = Decoder(W, shape, precision=args.precision, block=32, max_batch=args.batch,
                   max_ctx=args.prompt + 32 * max(total_rounds, 70) + 64, kv_chunk=args.kv_chunk)
     print(f"[bench] setup {time.perf_counter() - t_setup:.1f}s", file=sys.stderr, flush=True)
+    if args.block != 32:
+        dec.set_block(args.block)
     dec.prefill(torch.from_numpy(prompts), max_out=32 * max(total_rounds, 70))
     torch.cuda.synchronize()
     g = dec.capture(dec.round_greedy)  # its warm-up call is one untimed round
@@ -906,7 +988,7 @@ def main():
         "dtype": args.precision,
         "data": "synthetic (seeded random-init weights N(0,0.02), diffusion view = AR + N(0,0.002), uniform prompt ids)",
         "config": {"workload": "Orthrus round, Qwen3-8B width truncated to %d layers, greedy" % shape.layers,
-                   "batch": args.batch, "prompt_len": args.prompt, "block": 32, "hidden": shape.hidden,
+                   "batch": args.batch, "prompt_len": args.prompt, "block": args.block, "hidden": shape.hidden,
                    "heads": f"{shape.q_heads}Q/{shape.kv_heads}KV x {shape.head_dim}", "inter": shape.inter,
                    "vocab": shape.vocab, "kv_chunk": args.kv_chunk, "parallelism": "single GPU"},
         "round_latency_ms": round(ms, 4),
