@@ -353,10 +353,12 @@ def lmhead_consensus_c4(replays=50):
     st_ls = alternating_ms([lambda: ora.lmhead_argmax(dd, hd_t, w_t, seqs, rnds, dtok, zd, ld, ws)], 10)
     ora.lmhead_argmax(dt_, h_t, w_t, seqs, rnds, tok, zt, lt, ws)
 
+    rws = torch.empty(max(16, ora.rejection_workspace_bytes(B, V)), dtype=torch.uint8, device="cuda")
+
     def rej():
         reset()
         ora.rejection_accept(B, K, V, T, 77, seqs, zd, zt, ld, lt, dtok, ctx, state["anchor"], state["accept"], outb,
-                             state["out_len"], rnds, done, 64, 1 << 30)
+                             state["out_len"], rnds, done, 64, 1 << 30, rws)
     st_r = alternating_ms([rej], replays)
     res["lmhead_sampled_with_logits_m512"] = {"ms_stats": rounded(st_ls),
                                               "note": "Gumbel-max sample + fp32 logits (311 MB) + logsumexp"}

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define ORTHRUS_ABI_VERSION 2
+#define ORTHRUS_ABI_VERSION 3
 
 typedef enum {
   ORTHRUS_OK = 0,
@@ -191,15 +191,22 @@ int32_t orthrus_consensus_commit(int32_t batch, int32_t block, const int32_t* dr
  * (from p_j if that has no mass) by exponential race argmax_x r(x) / E_x, E_x = -ln u_x with
  * u_x from (seed, RESID), counter (x/4, 0, round[b], seq_id[b]), word x%4; ties -> lowest id.
  * A draft id outside [0, vocab) is rejected at its slot without reading its logits.
- * Then the same commit as orthrus_consensus_commit.  One workgroup per sequence; no workspace.
+ * Then the same commit as orthrus_consensus_commit.
+ * Two launches: the race over the rejected row in 2048-entry vocabulary chunks (one workgroup
+ * each, grid batch x chunks), then one wavefront per sequence that takes the maximum over the
+ * chunks and commits; the draw does not depend on the chunking (the maximum is exact).
+ * Workspace: orthrus_rejection_workspace_bytes(batch, vocab) bytes (16 per chunk per sequence),
+ * caller-owned, contents undefined on entry and exit; calls that overlap on one workspace race.
  * ------------------------------------------------------------------------------------------ */
+size_t orthrus_rejection_workspace_bytes(int32_t batch, int32_t vocab);
 int32_t orthrus_rejection_accept(int32_t batch, int32_t block, int32_t vocab, float temperature,
                                  uint64_t seed, const int32_t* seq_id, const float* draft_logits,
                                  const float* target_logits, const float* draft_lse,
                                  const float* target_lse, const int32_t* draft, int32_t* ctx_len,
                                  int32_t* anchor, int32_t* accept, int32_t* out_tokens,
                                  int32_t* out_len, int32_t* round, int32_t* done, int32_t max_out,
-                                 int32_t max_ctx, void* stream);
+                                 int32_t max_ctx, void* workspace, size_t workspace_bytes,
+                                 void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * Support kernels for the decoder layers of both views.

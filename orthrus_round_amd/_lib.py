@@ -56,8 +56,9 @@ _SIGS = {
     "orthrus_consensus_commit": ([_I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P], _I32),
     "orthrus_draft_fill": ([_I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _I32, _I32, _P, _P, _P], _I32),
     "orthrus_draft_merge": ([_I32, _I32, _P, _P, _P, _P, _P], _I32),
+    "orthrus_rejection_workspace_bytes": ([_I32, _I32], _SZ),
     "orthrus_rejection_accept": ([_I32, _I32, _I32, _F32, _U64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                  _P, _P, _I32, _I32, _P], _I32),
+                                  _P, _P, _I32, _I32, _P, _SZ, _P], _I32),
     "orthrus_gemm_workspace_bytes": ([_I32, _I32, _I32, _I32, _I32], _SZ),
     "orthrus_gemm": ([_I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P], _I32),
     "orthrus_gemm_rope_kv_write": ([_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I32, _P,
@@ -175,13 +176,18 @@ def draft_merge(batch, block, filled, tokens2, draft2, draft_out, stream=None):
                                      _stream(stream)))
 
 
+def rejection_workspace_bytes(batch, vocab) -> int:
+    return lib().orthrus_rejection_workspace_bytes(batch, vocab)
+
+
 def rejection_accept(batch, block, vocab, temperature, seed, seq_id, draft_logits, target_logits, draft_lse,
                      target_lse, draft, ctx_len, anchor, accept, out_tokens, out_len, round_, done, max_out,
-                     max_ctx, stream=None):
+                     max_ctx, ws, stream=None):
     _check(lib().orthrus_rejection_accept(batch, block, vocab, temperature, seed, _ptr(seq_id), _ptr(draft_logits),
                                           _ptr(target_logits), _ptr(draft_lse), _ptr(target_lse), _ptr(draft),
                                           _ptr(ctx_len), _ptr(anchor), _ptr(accept), _ptr(out_tokens),
-                                          _ptr(out_len), _ptr(round_), _ptr(done), max_out, max_ctx,
+                                          _ptr(out_len), _ptr(round_), _ptr(done), max_out, max_ctx, _ptr(ws),
+                                          0 if ws is None or isinstance(ws, int) else ws.numel() * ws.element_size(),
                                           _stream(stream)))
 
 

@@ -64,86 +64,133 @@ __global__ __launch_bounds__(64) void consensus_kernel(int K, const int32_t* __r
   commit_tokens(cs, b, K, k, count, my_tok, last_tok, lane);
 }
 
-// One workgroup per sequence.
-__global__ __launch_bounds__(256) void rejection_kernel(int K, int V, float inv_t, uint64_t seed,
-                                                        const int32_t* __restrict__ seq_id,
-                                                        const float* __restrict__ zd, const float* __restrict__ zt,
-                                                        const float* __restrict__ lse_d,
-                                                        const float* __restrict__ lse_t,
-                                                        const int32_t* __restrict__ draft, CommitState cs) {
-  __shared__ uint64_t red[4];
-  __shared__ int s_any[4];
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+// The rejection accept runs in two launches.  The residual draw needs one Philox call per four
+// vocabulary entries of the first rejected row, so it is spread over kRaceChunk-entry chunks
+// (one workgroup each, grid chunks x batch); every chunk leaves the packed maximum of its race
+// keys for the residual and for the fallback law p (grid batch x chunks, so the batch is not
+// limited by the grid's second dimension).  A one-wavefront launch per sequence then
+// takes the maximum over the chunks (exact and order-free, so the draw does not depend on the
+// chunking) and commits.  Both launches recompute the accepted prefix k from the same inputs.
+constexpr int kRaceThreads = 256;
+constexpr int kRaceChunk = 2048;  // vocabulary entries per race workgroup
+
+__host__ __device__ constexpr int race_chunks(int vocab) { return (vocab + kRaceChunk - 1) / kRaceChunk; }
+
+// Leading accepted drafts of sequence b: slot i accepts iff u_i * q_i(d_i) < p_i(d_i).  Called by
+// one full wavefront; every lane gets k.
+__device__ __forceinline__ int accepted_prefix(int b, int K, int V, float inv_t, uint64_t seed, int rnd, int sid,
+                                               const float* __restrict__ zd, const float* __restrict__ zt,
+                                               const float* __restrict__ lse_d, const float* __restrict__ lse_t,
+                                               const int32_t* __restrict__ draft, int lane) {
+  bool acc = true;
+  if (lane < K) {
+    const int d = draft[(size_t)b * K + lane];
+    const size_t row = (size_t)b * K + lane;
+    if (d >= 0 && d < V) {
+      const float q = expf(zd[row * V + d] * inv_t - lse_d[row]);
+      const float p = expf(zt[row * V + d] * inv_t - lse_t[row]);
+      const float u = philox_uniform(seed, ORTHRUS_STREAM_ACCEPT, lane, 0, rnd, sid);
+      acc = u * q < p;
+    } else {
+      acc = false;  // an id outside the vocabulary is never accepted (and never read)
+    }
+  }
+  const uint64_t rej = __ballot(lane < K && !acc);
+  return rej ? __builtin_ctzll(rej) : K;
+}
+
+// Race keys over one chunk of the first rejected row: r(x) / E_x with E_x = -ln u_x, for the
+// residual r = max(0, p - q) and for p itself.  part[b, chunk] = {residual max, p max} (0: no mass).
+__global__ __launch_bounds__(kRaceThreads) void rejection_race_kernel(
+    int K, int V, float inv_t, uint64_t seed, const int32_t* __restrict__ seq_id, const float* __restrict__ zd,
+    const float* __restrict__ zt, const float* __restrict__ lse_d, const float* __restrict__ lse_t,
+    const int32_t* __restrict__ draft, const int32_t* __restrict__ done, const int32_t* __restrict__ round,
+    ulonglong2* __restrict__ part) {
+  __shared__ int s_k;
+  __shared__ uint64_t red[2][kRaceThreads / kWave];
+  const int b = blockIdx.x, chunk = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (done[b] != 0) return;
+  const int rnd = round[b], sid = seq_id[b];
+  if (w == 0) {
+    const int k = accepted_prefix(b, K, V, inv_t, seed, rnd, sid, zd, zt, lse_d, lse_t, draft, lane);
+    if (lane == 0) s_k = k;
+  }
+  __syncthreads();
+  const int k = s_k;
+  if (k >= K) return;  // every draft accepted: nothing to draw
+  const size_t row = (size_t)b * K + k;
+  const float ld = lse_d[row], lt = lse_t[row];
+  const float* zdr = zd + row * V;
+  const float* ztr = zt + row * V;
+  uint64_t best_r = 0, best_p = 0;
+  const int x_end = min(V, (chunk + 1) * kRaceChunk);
+  for (int x0 = chunk * kRaceChunk + tid * 4; x0 < x_end; x0 += kRaceThreads * 4) {
+    const u64x4 wd = philox4x64_10((uint64_t)(x0 >> 2), 0, (uint64_t)rnd, (uint64_t)sid, seed, ORTHRUS_STREAM_RESID);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int x = x0 + e;
+      if (x >= x_end) break;
+      const float p = expf(ztr[x] * inv_t - lt);
+      const float rr = fmaxf(p - expf(zdr[x] * inv_t - ld), 0.0f);
+      if (p > 0.0f) {
+        const float E = -logf(word_to_uniform(wd.x[e]));
+        best_p = umax64(best_p, pack_argmax(p / E, x));
+        if (rr > 0.0f) best_r = umax64(best_r, pack_argmax(rr / E, x));
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    best_r = umax64(best_r, shfl_xor_u64(best_r, off));
+    best_p = umax64(best_p, shfl_xor_u64(best_p, off));
+  }
+  if (lane == 0) { red[0][w] = best_r; red[1][w] = best_p; }
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t r = 0, q = 0;
+#pragma unroll
+    for (int i = 0; i < kRaceThreads / kWave; ++i) { r = umax64(r, red[0][i]); q = umax64(q, red[1][i]); }
+    part[(size_t)b * gridDim.y + chunk] = make_ulonglong2(r, q);
+  }
+}
+
+// One wavefront per sequence: the accepted prefix, the residual draw (maximum over the chunks'
+// keys; the law p if the residual has no mass anywhere) and the commit.
+__global__ __launch_bounds__(64) void rejection_commit_kernel(int K, int V, int nchunks, float inv_t, uint64_t seed,
+                                                              const int32_t* __restrict__ seq_id,
+                                                              const float* __restrict__ zd,
+                                                              const float* __restrict__ zt,
+                                                              const float* __restrict__ lse_d,
+                                                              const float* __restrict__ lse_t,
+                                                              const int32_t* __restrict__ draft,
+                                                              const ulonglong2* __restrict__ part, CommitState cs) {
+  const int b = blockIdx.x, lane = threadIdx.x;
   if (cs.done[b] != 0) {
-    if (tid == 0) cs.accept[b] = -1;
+    if (lane == 0) cs.accept[b] = -1;
     return;
   }
   const int rnd = cs.round[b], sid = seq_id[b];
-  // acceptance of slot i: u_i * q_i(d_i) < p_i(d_i)
-  int k;
-  {
-    bool acc = true;
-    int d = 0;
-    if (lane < K) {
-      d = draft[(size_t)b * K + lane];
-      const size_t row = (size_t)b * K + lane;
-      if (d >= 0 && d < V) {
-        const float q = expf(zd[row * V + d] * inv_t - lse_d[row]);
-        const float p = expf(zt[row * V + d] * inv_t - lse_t[row]);
-        const float u = philox_uniform(seed, ORTHRUS_STREAM_ACCEPT, lane, 0, rnd, sid);
-        acc = u * q < p;
-      } else {
-        acc = false;  // an id outside the vocabulary is never accepted (and never read)
-      }
-    }
-    const uint64_t rej = __ballot(lane < K && !acc);
-    k = rej ? __builtin_ctzll(rej) : K;
-  }
+  const int k = accepted_prefix(b, K, V, inv_t, seed, rnd, sid, zd, zt, lse_d, lse_t, draft, lane);
   int corr = 0;
   if (k < K) {
-    // residual race over the vocabulary for slot k: argmax_x r(x) / E_x, E_x = -ln u_x
-    const size_t row = (size_t)b * K + k;
-    const float ld = lse_d[row], lt = lse_t[row];
-    const float* zdr = zd + row * V;
-    const float* ztr = zt + row * V;
-    for (int pass = 0; pass < 2; ++pass) {
-      uint64_t best = 0;
-      int any = 0;
-      for (int x0 = tid * 4; x0 < V; x0 += 256 * 4) {
-        const u64x4 wd = philox4x64_10((uint64_t)(x0 >> 2), 0, (uint64_t)rnd, (uint64_t)sid, seed, ORTHRUS_STREAM_RESID);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int x = x0 + e;
-          if (x >= V) break;
-          const float p = expf(ztr[x] * inv_t - lt);
-          float rr;
-          if (pass == 0) rr = fmaxf(p - expf(zdr[x] * inv_t - ld), 0.0f);
-          else rr = p;  // residual had no mass: fall back to p
-          if (rr > 0.0f) {
-            any = 1;
-            const float E = -logf(word_to_uniform(wd.x[e]));
-            best = umax64(best, pack_argmax(rr / E, x));
-          }
-        }
-      }
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) best = umax64(best, shfl_xor_u64(best, off));
-      any = __any(any);
-      if (lane == 0) { red[w] = best; s_any[w] = any; }
-      __syncthreads();
-      best = umax64(umax64(red[0], red[1]), umax64(red[2], red[3]));
-      any = s_any[0] | s_any[1] | s_any[2] | s_any[3];
-      __syncthreads();
-      if (any || pass == 1) { corr = unpack_idx(best); break; }
+    uint64_t r = 0, q = 0;
+    for (int c = lane; c < nchunks; c += 64) {
+      const ulonglong2 v = part[(size_t)b * nchunks + c];
+      r = umax64(r, v.x);
+      q = umax64(q, v.y);
     }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      r = umax64(r, shfl_xor_u64(r, off));
+      q = umax64(q, shfl_xor_u64(q, off));
+    }
+    corr = unpack_idx(r != 0 ? r : q);
   }
-  if (w == 0) {
-    const int count = min(k + 1, K);
-    const int d = lane < K ? draft[(size_t)b * K + lane] : 0;
-    const int my_tok = lane < k ? d : corr;
-    const int last_tok = __shfl(my_tok, count - 1, 64);
-    commit_tokens(cs, b, K, k, count, my_tok, last_tok, lane);
-  }
+  const int count = min(k + 1, K);
+  const int d = lane < K ? draft[(size_t)b * K + lane] : 0;
+  const int my_tok = lane < k ? d : corr;
+  const int last_tok = __shfl(my_tok, count - 1, 64);
+  commit_tokens(cs, b, K, k, count, my_tok, last_tok, lane);
 }
 
 __global__ void philox_kernel(int64_t n, const uint64_t* ctr, uint64_t k0, uint64_t k1, uint64_t* out) {
@@ -257,13 +304,18 @@ extern "C" int32_t orthrus_consensus_commit(int32_t batch, int32_t block, const 
   return check_launch("orthrus_consensus_commit");
 }
 
+extern "C" size_t orthrus_rejection_workspace_bytes(int32_t batch, int32_t vocab) {
+  if (batch <= 0 || vocab <= 0) return 0;
+  return (size_t)batch * race_chunks(vocab) * sizeof(ulonglong2);
+}
+
 extern "C" int32_t orthrus_rejection_accept(int32_t batch, int32_t block, int32_t vocab, float temperature,
                                             uint64_t seed, const int32_t* seq_id, const float* draft_logits,
                                             const float* target_logits, const float* draft_lse,
                                             const float* target_lse, const int32_t* draft, int32_t* ctx_len,
                                             int32_t* anchor, int32_t* accept, int32_t* out_tokens, int32_t* out_len,
                                             int32_t* round, int32_t* done, int32_t max_out, int32_t max_ctx,
-                                            void* stream) {
+                                            void* workspace, size_t workspace_bytes, void* stream) {
   if (int32_t s = check_state(batch, block, ctx_len, anchor, accept, out_tokens, out_len, round, done, max_out, max_ctx))
     return s;
   ORTHRUS_REQUIRE(vocab > 0 && temperature > 0.0f && std::isfinite(temperature), ORTHRUS_ERR_INVALID_ARG,
@@ -271,9 +323,20 @@ extern "C" int32_t orthrus_rejection_accept(int32_t batch, int32_t block, int32_
   ORTHRUS_REQUIRE(seq_id && draft_logits && target_logits && draft_lse && target_lse && draft, ORTHRUS_ERR_INVALID_ARG,
                   "rejection: null pointer");
   if (batch == 0) return ORTHRUS_OK;
+  const size_t need = orthrus_rejection_workspace_bytes(batch, vocab);
+  ORTHRUS_REQUIRE(workspace && workspace_bytes >= need, ORTHRUS_ERR_WORKSPACE,
+                  "rejection: workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
+  const int nchunks = race_chunks(vocab);
+  ORTHRUS_REQUIRE(nchunks <= 65535, ORTHRUS_ERR_UNSUPPORTED, "rejection: vocab %d above %d", vocab, 65535 * kRaceChunk);
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  auto* part = static_cast<ulonglong2*>(workspace);
+  const float inv_t = 1.0f / temperature;
+  hipLaunchKernelGGL(rejection_race_kernel, dim3(batch, nchunks), dim3(kRaceThreads), 0, st, block, vocab, inv_t,
+                     seed, seq_id, draft_logits, target_logits, draft_lse, target_lse, draft, done, round, part);
+  if (int32_t s = check_launch("orthrus_rejection_accept (race)")) return s;
   CommitState cs{ctx_len, anchor, accept, out_tokens, out_len, round, done, max_out, max_ctx};
-  hipLaunchKernelGGL(rejection_kernel, dim3(batch), dim3(256), 0, reinterpret_cast<hipStream_t>(stream), block, vocab,
-                     1.0f / temperature, seed, seq_id, draft_logits, target_logits, draft_lse, target_lse, draft, cs);
+  hipLaunchKernelGGL(rejection_commit_kernel, dim3(batch), dim3(64), 0, st, block, vocab, nchunks, inv_t, seed, seq_id,
+                     draft_logits, target_logits, draft_lse, target_lse, draft, part, cs);
   return check_launch("orthrus_rejection_accept");
 }
 

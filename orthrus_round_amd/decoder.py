@@ -308,6 +308,8 @@ class Decoder:
             M = B * K
             self._logits = [torch.empty((M, s.vocab), dtype=torch.float32, device=self.dev) for _ in range(2)]
             self._lse = [torch.empty(M, dtype=torch.float32, device=self.dev) for _ in range(2)]
+            self._rej_ws = torch.empty(max(16, L.rejection_workspace_bytes(B, s.vocab)),
+                                       dtype=torch.uint8, device=self.dev)
         L.embed_block(B, K, s.hidden, self.dt, self.embed, self.anchor, None, 0, 0, s.mask_id, self.x)
         self._layers("diff", B, K, self.ctx_len, draft=True)
         self._lm_head(B, K, self.draft, temperature, seed, L.STREAM_DRAFT, self._logits[0], self._lse[0])
@@ -317,7 +319,8 @@ class Decoder:
         self._lm_head(B, K, self.target, temperature, seed, L.STREAM_AR, self._logits[1], self._lse[1], sample=False)
         L.rejection_accept(B, K, s.vocab, temperature, seed, self.seq_id, self._logits[0], self._logits[1],
                            self._lse[0], self._lse[1], self.draft, self.ctx_len, self.anchor, self.accept,
-                           self.out_tokens, self.out_len, self.round, self.done, self.max_out, self.max_ctx)
+                           self.out_tokens, self.out_len, self.round, self.done, self.max_out, self.max_ctx,
+                           self._rej_ws)
 
     def ar_step(self, temperature: float = 0.0, seed: int = 0, logits: torch.Tensor | None = None):
         """One plain AR step for every sequence: a one-row causal pass, argmax/sample, commit.

@@ -66,6 +66,10 @@ def test_struct_layouts_match_header():
     (lambda: ora.draft_merge(2, 32, 1, 1, None, 1, stream=0), 1),
     (lambda: ora.draft_merge(-1, 32, 1, 1, 1, 1, stream=0), 1),
     (lambda: ora.rmsnorm(2, 64, 7, 1, 1, 1e-6, 1, stream=0), 1),
+    (lambda: ora.rejection_accept(2, 32, 1000, 0.8, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 8, 64, None,
+                                  stream=0), 3),  # no workspace
+    (lambda: ora.rejection_accept(2, 32, 1000, 0.0, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 8, 64, 1,
+                                  stream=0), 1),  # temperature 0
     (lambda: ora.rope_table(0, 64, 1e6, 1, stream=0), 1),
 ])
 def test_validation_errors_before_launch(call, status):
@@ -100,3 +104,10 @@ def test_gemm_workspace_holds_the_k_quarter_partials():
     assert ora.gemm_workspace_bytes(8, 24576, 4096, ora.BF16, ora.EPI_SWIGLU) == 0
     assert ora.gemm_workspace_bytes(8, 4096, 192, ora.BF16, ora.EPI_STORE) == 0
     assert ora.gemm_workspace_bytes(0, 4096, 4096, ora.BF16, ora.EPI_STORE) == 0
+
+
+def test_rejection_workspace_holds_one_pair_per_vocabulary_chunk():
+    # two packed race maxima (16 bytes) per 2048-entry chunk of the vocabulary, per sequence
+    assert ora.rejection_workspace_bytes(16, 151936) == 16 * 75 * 16
+    assert ora.rejection_workspace_bytes(1, 2048) == 16 and ora.rejection_workspace_bytes(1, 2049) == 32
+    assert ora.rejection_workspace_bytes(0, 151936) == 0

@@ -269,8 +269,9 @@ def test_rejection_accept_matches_oracle(V, mix):
     rnd_t = dev(rnds.copy())
     ctx = torch.full((B,), 500, dtype=torch.int32, device=DEV)
     out = torch.full((B, 64), -1, dtype=torch.int32, device=DEV)
+    rws = torch.empty(ora.rejection_workspace_bytes(B, V), dtype=torch.uint8, device=DEV)
     ora.rejection_accept(B, K, V, T, seed, dev(seqs), zd_t, zt_t, ld, lt, dt, ctx, st["anchor"], st["accept"], out,
-                         st["out_len"], rnd_t, st["done"], 64, 100000)
+                         st["out_len"], rnd_t, st["done"], 64, 100000, rws)
     torch.cuda.synchronize()
     acc = st["accept"].cpu().numpy()
     outn = out.cpu().numpy()

@@ -37,8 +37,9 @@ def state(B, ctx0=500, max_out=64):
 
 
 def reject(B, K, V, T, seed, seqs, zd, zt, ld, lt, d, s, max_out=64, max_ctx=1 << 30):
+    ws = torch.empty(max(16, ora.rejection_workspace_bytes(B, V)), dtype=torch.uint8, device=DEV)
     ora.rejection_accept(B, K, V, T, seed, seqs, zd, zt, ld, lt, d, s["ctx"], s["anchor"], s["accept"], s["out"],
-                         s["out_len"], s["round"], s["done"], max_out, max_ctx)
+                         s["out_len"], s["round"], s["done"], max_out, max_ctx, ws)
     torch.cuda.synchronize()
 
 
@@ -124,10 +125,12 @@ def test_rejection_kernel_output_law_tiny_vocab():
     assert np.array_equal(out[acc == 1], drafts[acc == 1])  # an accept commits the draft
 
 
-def test_rejection_rejects_out_of_range_draft_ids():
+@pytest.mark.parametrize("V", [50, 5000])
+def test_rejection_rejects_out_of_range_draft_ids(V):
     """A draft id outside [0, V) is rejected at its slot without reading its logits; the slots before
-    it (q = p, so always accepted) are committed and the correction is drawn from p at that slot."""
-    B, K, V, T, seed = 3, 6, 50, 0.8, 7
+    it (q = p, so always accepted) are committed and the correction is drawn from p at that slot
+    (the residual has no mass).  V = 5000 spans three race chunks with a ragged last one."""
+    B, K, T, seed = 3, 6, 0.8, 7
     rs = np.random.default_rng(3)
     z = rs.standard_normal((B, K, V)).astype(np.float32) * 2
     lse = sp.logsumexp(z.astype(np.float64) / T, axis=-1).astype(np.float32)
