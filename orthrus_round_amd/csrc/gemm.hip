@@ -85,7 +85,7 @@ __global__ __launch_bounds__(Cfg::NT) ORTHRUS_GEMM_WAVES void gemm_quarter_kerne
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int mtiles = (M + Cfg::BM - 1) / Cfg::BM;
   int q, mt, nt;
-  xcd_tile_map(blockIdx.x, gridDim.x, S, mtiles, q, mt, nt);
+  xcd_tile_map_ksplit(blockIdx.x, gridDim.x, S, mtiles, q, mt, nt);
   const int m0 = mt * Cfg::BM, n0 = nt * Cfg::BN, kq = K / S;
   f32x16 acc[Cfg::TM][Cfg::TN];
   gemm_mainloop<T, Cfg>(A + (size_t)q * kq, W + (size_t)q * kq, M, N, K, m0, n0, smem, acc, kq);

@@ -81,7 +81,7 @@ struct KsCfg : StageRings<T, BM_, BN_, SA_, SW_, 4> {
 
 // Map the linear workgroup id to (split, m_tile, n_tile) so that the splits and m-tiles sharing
 // a slice of W run back to back on the same XCD (workgroups are dealt round-robin to the 8 XCDs,
-// each with its own L2): W then comes from HBM once and split partials stay in that L2.
+// each with its own L2): W then comes from HBM once.
 // XCD x receives ids x, x+8, ...; with total = 8q + r the first r XCDs get q+1 of them, and XCD x
 // takes the contiguous logical range starting at x*q + min(x, r), so the map is a bijection.
 __device__ __forceinline__ int xcd_linear(int id, int total) {
@@ -93,6 +93,20 @@ __device__ __forceinline__ void xcd_tile_map(int id, int total, int splits, int 
   int L = xcd_linear(id, total);
   s = L % splits;
   L /= splits;
+  mt = L % mtiles;
+  nt = L / mtiles;
+}
+
+// The k-split variant: the split index varies slowest, so each XCD works on one slice of K (or
+// one of its halves' tiles) and fetches only that slice of the activation, instead of all of it
+// on every XCD; within a slice the m-tiles sharing a slice of W still run back to back.  Only the
+// placement changes: each (split, m_tile, n_tile) is computed exactly as before.
+__device__ __forceinline__ void xcd_tile_map_ksplit(int id, int total, int splits, int mtiles, int& s, int& mt,
+                                                    int& nt) {
+  const int per_split = total / splits;  // total = splits * mtiles * ntiles
+  int L = xcd_linear(id, total);
+  s = L / per_split;
+  L -= s * per_split;
   mt = L % mtiles;
   nt = L / mtiles;
 }
