@@ -138,7 +138,8 @@ __device__ __forceinline__ float word_to_uniform(uint64_t w) {
 __device__ __forceinline__ float philox_uniform(uint64_t seed, uint64_t stream, int64_t index, int64_t c1,
                                                 int64_t c2, int64_t c3) {
   u64x4 w = philox4x64_10((uint64_t)(index >> 2), (uint64_t)c1, (uint64_t)c2, (uint64_t)c3, seed, stream);
-  return word_to_uniform(w.x[index & 3]);
+  const int k = (int)(index & 3);  // selects, not a runtime array index (which would go to scratch)
+  return word_to_uniform(k == 0 ? w.x[0] : k == 1 ? w.x[1] : k == 2 ? w.x[2] : w.x[3]);
 }
 
 // ---------------------------------------------------------------------------------------

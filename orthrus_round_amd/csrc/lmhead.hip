@@ -70,48 +70,91 @@ __global__ __launch_bounds__(Cfg::NT) ORTHRUS_GEMM_WAVES void lmhead_kernel(LmAr
   float2* red_lse = reinterpret_cast<float2*>(red_best + Cfg::BM * Cfg::WN);  // [BM][NG]
   constexpr float kNegInf = -__builtin_huge_valf();
 
+  // One output element (accumulator i, register e, column tile j) of a row: logits store, token
+  // key, logsumexp group partial.  `u` is the element's uniform when sampling.
+  auto element = [&](int i, int e, int j, int m, bool mok, float u, uint64_t& best) {
+    const int mrow = (wm * Cfg::TM + i) * 32 + acc_row(e, hh);
+    const int n = n0 + (wn * Cfg::TN + j) * 32 + r;
+    const bool ok = mok && n < a.N;
+    const float z = acc[i][j][e];
+    if (ok && a.logits) a.logits[(size_t)m * a.N + n] = z;
+    float key = z;
+    if constexpr (kSample) key = z * a.inv_t - logf(-logf(u));
+    if (ok) best = umax64(best, pack_argmax(key, n));
+    if constexpr (kLse) {
+      const float zt = ok ? z * a.inv_t : kNegInf;
+      float gm = zt;
 #pragma unroll
-  for (int i = 0; i < Cfg::TM; ++i) {
+      for (int off = 1; off < 32; off <<= 1) gm = fmaxf(gm, shfl_xor_f(gm, off));
+      float gs = ok ? expf(zt - gm) : 0.0f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int mrow = (wm * Cfg::TM + i) * 32 + acc_row(e, hh);
-      const int m = m0 + mrow;
-      const bool mok = m < a.M;
-      int32_t rnd = 0, sid = 0, slot = 0;
-      if (kSample && mok) {
-        const int bseq = m / a.block;
-        slot = m % a.block;
-        rnd = a.round[bseq];
-        sid = a.seq_id[bseq];
-      }
-      uint64_t best = 0;
+      for (int off = 1; off < 32; off <<= 1) gs += shfl_xor_f(gs, off);
+      if (r == 0) red_lse[mrow * NG + wn * Cfg::TN + j] = make_float2(gm, gs);
+    }
+  };
+  // reduce a row's choice over the 32 columns held by this half-wave
+  auto finish_row = [&](int i, int e, uint64_t best) {
 #pragma unroll
-      for (int j = 0; j < Cfg::TN; ++j) {
-        const int n = n0 + (wn * Cfg::TN + j) * 32 + r;
-        const bool ok = mok && n < a.N;
-        const float z = acc[i][j][e];
-        if (ok && a.logits) a.logits[(size_t)m * a.N + n] = z;
-        float key = z;
-        if constexpr (kSample) {
-          const float u = philox_uniform(a.seed, a.stream_id, slot, n, rnd, sid);
-          key = z * a.inv_t - logf(-logf(u));
+    for (int off = 1; off < 32; off <<= 1) best = umax64(best, shfl_xor_u64(best, off));
+    if (r == 0) red_best[((wm * Cfg::TM + i) * 32 + acc_row(e, hh)) * Cfg::WN + wn] = best;
+  };
+
+  if (kSample && a.block % 4 == 0) {
+    // Registers 4q..4q+3 of a lane hold four consecutive rows, one aligned group of four block slots
+    // of one sequence; the four words of the Philox call with counter (slot/4, n, round, seq) are
+    // exactly their four uniforms, so one call serves the four rows.
+    // compile-time loops: the accumulator registers must be indexed by constants
+    static_for<Cfg::TM>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      static_for<4>([&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        const int mb = m0 + (wm * Cfg::TM + i) * 32 + acc_row(4 * q, hh);  // first of the four rows
+        uint64_t c0 = 0, c2 = 0, c3 = 0;
+        if (mb < a.M) {
+          const int bseq = mb / a.block;
+          c0 = (uint64_t)((mb % a.block) >> 2);
+          c2 = (uint64_t)a.round[bseq];
+          c3 = (uint64_t)a.seq_id[bseq];
         }
-        if (ok) best = umax64(best, pack_argmax(key, n));
-        if constexpr (kLse) {
-          const float zt = ok ? z * a.inv_t : kNegInf;
-          float gm = zt;
+        uint64_t best0 = 0, best1 = 0, best2 = 0, best3 = 0;
+        static_for<Cfg::TN>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          const int n = n0 + (wn * Cfg::TN + j) * 32 + r;
+          const u64x4 wd = philox4x64_10(c0, (uint64_t)n, c2, c3, a.seed, a.stream_id);
+          element(i, 4 * q + 0, j, mb + 0, mb + 0 < a.M, word_to_uniform(wd.x[0]), best0);
+          element(i, 4 * q + 1, j, mb + 1, mb + 1 < a.M, word_to_uniform(wd.x[1]), best1);
+          element(i, 4 * q + 2, j, mb + 2, mb + 2 < a.M, word_to_uniform(wd.x[2]), best2);
+          element(i, 4 * q + 3, j, mb + 3, mb + 3 < a.M, word_to_uniform(wd.x[3]), best3);
+        });
+        finish_row(i, 4 * q + 0, best0);
+        finish_row(i, 4 * q + 1, best1);
+        finish_row(i, 4 * q + 2, best2);
+        finish_row(i, 4 * q + 3, best3);
+      });
+    });
+  } else {
 #pragma unroll
-          for (int off = 1; off < 32; off <<= 1) gm = fmaxf(gm, shfl_xor_f(gm, off));
-          float gs = ok ? expf(zt - gm) : 0.0f;
+    for (int i = 0; i < Cfg::TM; ++i) {
 #pragma unroll
-          for (int off = 1; off < 32; off <<= 1) gs += shfl_xor_f(gs, off);
-          if (r == 0) red_lse[mrow * NG + wn * Cfg::TN + j] = make_float2(gm, gs);
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + (wm * Cfg::TM + i) * 32 + acc_row(e, hh);
+        const bool mok = m < a.M;
+        int32_t rnd = 0, sid = 0, slot = 0;
+        if (kSample && mok) {
+          const int bseq = m / a.block;
+          slot = m % a.block;
+          rnd = a.round[bseq];
+          sid = a.seq_id[bseq];
         }
-      }
-      // reduce over the 32 columns held by this half-wave (same rows)
+        uint64_t best = 0;
 #pragma unroll
-      for (int off = 1; off < 32; off <<= 1) best = umax64(best, shfl_xor_u64(best, off));
-      if (r == 0) red_best[mrow * Cfg::WN + wn] = best;
+        for (int j = 0; j < Cfg::TN; ++j) {
+          float u = 0.0f;
+          if constexpr (kSample) u = philox_uniform(a.seed, a.stream_id, slot, n0 + (wn * Cfg::TN + j) * 32 + r, rnd, sid);
+          element(i, e, j, m, mok, u, best);
+        }
+        finish_row(i, e, best);
+      }
     }
   }
   __syncthreads();

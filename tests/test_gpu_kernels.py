@@ -155,16 +155,20 @@ def test_lmhead_lse_is_optional_and_temperature_scaled(c4):
     assert np.abs(lse3 - lse).max() > 0.1  # the temperature is applied
 
 
-def test_lmhead_gumbel_sampling_matches_oracle():
+@pytest.mark.parametrize("M,block", [(64, 32), (40, 4), (60, 6), (7, 1)])
+def test_lmhead_gumbel_sampling_matches_oracle(M, block):
+    """Blocks that are a multiple of 4 take one Philox call per four rows of a lane (its four
+    words); other blocks one call per element.  Both must draw the oracle's uniforms."""
     T, seed = 0.8, 1234
-    h, w = synth.lmhead_inputs(9, 64, 256, 4096, bf16=False)
-    seqs = np.array([5, 9], np.int32)
-    rnds = np.array([3, 0], np.int32)
-    tok, lse, _ = lmhead(h, w, ora.F32, temperature=T, seed=seed, block=32, seq=seqs, rnd=rnds)
+    h, w = synth.lmhead_inputs(9, M, 256, 4096, bf16=False)
+    nseq = M // block
+    seqs = (np.arange(nseq, dtype=np.int32) * 4 + 5)
+    rnds = (np.arange(nseq, dtype=np.int32) * 3) % 7
+    tok, lse, _ = lmhead(h, w, ora.F32, temperature=T, seed=seed, block=block, seq=seqs, rnd=rnds)
     z = h.astype(np.float64) @ w.astype(np.float64).T
     amb = 0
-    for r in range(64):
-        b, s = divmod(r, 32)
+    for r in range(M):
+        b, s = divmod(r, block)
         u = P.uniforms(seed, P.STREAM_DRAFT, s, np.arange(4096), rnds[b], seqs[b])
         key = z[r] / T - np.log(-np.log(u))
         ok, a = tie_ok(key, tok[r], int(np.argmax(key)))

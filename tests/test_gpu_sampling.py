@@ -100,10 +100,10 @@ def test_rejection_accept_qwen3_8b_shape():
 
 
 def test_rejection_kernel_output_law_tiny_vocab():
-    """V = 8, 200000 seeded sequences with one slot each, drafts drawn from q on the host: the
+    """V = 8, 10^6 seeded sequences with one slot each, drafts drawn from q on the host: the
     device accepts with probability sum_x min(p, q) and commits tokens distributed as p
     (p = softmax(z_target/T), q = softmax(z_draft/T) from scipy)."""
-    B, V, T, seed = 200_000, 8, 0.8, 2024
+    B, V, T, seed = 1_000_000, 8, 0.8, 2024
     zt1 = np.array([1.2, -0.3, 0.4, 2.0, -1.1, 0.1, 0.7, -0.6])
     zd1 = np.array([0.2, 0.9, 0.4, 1.1, -0.2, 0.8, -0.5, 0.3])
     p, q = sp.softmax(zt1 / T), sp.softmax(zd1 / T)
