@@ -196,7 +196,8 @@ int32_t orthrus_consensus_commit(int32_t batch, int32_t block, const int32_t* dr
  * each, grid batch x chunks), then one wavefront per sequence that takes the maximum over the
  * chunks and commits; the draw does not depend on the chunking (the maximum is exact).
  * Workspace: orthrus_rejection_workspace_bytes(batch, vocab) bytes (16 per chunk per sequence),
- * caller-owned, contents undefined on entry and exit; calls that overlap on one workspace race.
+ * 16-byte aligned, caller-owned, contents undefined on entry and exit; calls that overlap on one
+ * workspace race.
  * ------------------------------------------------------------------------------------------ */
 size_t orthrus_rejection_workspace_bytes(int32_t batch, int32_t vocab);
 int32_t orthrus_rejection_accept(int32_t batch, int32_t block, int32_t vocab, float temperature,

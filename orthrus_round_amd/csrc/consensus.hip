@@ -326,6 +326,8 @@ extern "C" int32_t orthrus_rejection_accept(int32_t batch, int32_t block, int32_
   const size_t need = orthrus_rejection_workspace_bytes(batch, vocab);
   ORTHRUS_REQUIRE(workspace && workspace_bytes >= need, ORTHRUS_ERR_WORKSPACE,
                   "rejection: workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
+  ORTHRUS_REQUIRE(((uintptr_t)workspace & 15) == 0, ORTHRUS_ERR_INVALID_ARG,
+                  "rejection: workspace must be 16-byte aligned");
   const int nchunks = race_chunks(vocab);
   ORTHRUS_REQUIRE(nchunks <= 65535, ORTHRUS_ERR_UNSUPPORTED, "rejection: vocab %d above %d", vocab, 65535 * kRaceChunk);
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);

@@ -106,6 +106,13 @@ def test_gemm_workspace_holds_the_k_quarter_partials():
     assert ora.gemm_workspace_bytes(0, 4096, 4096, ora.BF16, ora.EPI_STORE) == 0
 
 
+def test_rejection_refuses_a_misaligned_workspace():
+    L = ora.lib()
+    args = [2, 32, 1000, 0.8, 1] + [16] * 13 + [8, 64]
+    st = L.orthrus_rejection_accept(*args, 24, 1 << 20, None)  # 24 is not a multiple of 16
+    assert st == 1 and b"aligned" in L.orthrus_last_error()
+
+
 def test_rejection_workspace_holds_one_pair_per_vocabulary_chunk():
     # two packed race maxima (16 bytes) per 2048-entry chunk of the vocabulary, per sequence
     assert ora.rejection_workspace_bytes(16, 151936) == 16 * 75 * 16
