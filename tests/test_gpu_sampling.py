@@ -149,3 +149,57 @@ def test_rejection_rejects_out_of_range_draft_ids(V):
         er = -np.log(P.uniforms(seed, P.STREAM_RESID, np.arange(V), 0, 0, b))
         corr = Dc.race(sp.softmax(z[b, j].astype(np.float64) / T), er)  # residual p - q = 0: drawn from p
         assert list(outn[b, :j + 1]) == list(d[b, :j]) + [corr]
+
+
+# ------------------------------------------------------------------- the round's output law
+
+MICRO = synth.ModelShape(layers=1, hidden=64, q_heads=2, kv_heads=1, head_dim=64, inter=128, vocab=8)
+
+
+def _chi2_pvalue(counts, probs, min_expected=5.0):
+    """Pearson chi-square p-value; cells expected below ``min_expected`` are pooled into one."""
+    counts = np.asarray(counts, dtype=np.float64).ravel()
+    probs = np.asarray(probs, dtype=np.float64).ravel()
+    exp = counts.sum() * probs
+    big = exp >= min_expected
+    c = np.append(counts[big], counts[~big].sum())
+    e = np.append(exp[big], exp[~big].sum())
+    if e[-1] == 0:
+        assert c[-1] == 0, "samples fell on cells of probability 0"
+        c, e = c[:-1], e[:-1]
+    return st.chi2.sf(((c - e) ** 2 / e).sum(), len(c) - 1)
+
+
+def test_sampled_round_follows_the_ar_law():
+    """Orthrus paper summary, sec. 四 and Q&A: with a temperature the committed tokens follow AR
+    sampling's distribution.  One batch of 6000 sequences with the same prompt (each its own
+    Philox stream through its sequence id) through a one-layer decoder on an 8-token vocabulary,
+    block 4, T = 0.8: the first two committed tokens of the device's Orthrus rounds and of its AR
+    steps both follow p(t1) p(t2 | t1) of the AR model (oracle passes, float64), and slot 0 is
+    accepted with probability sum_x min(p, q)."""
+    W = synth.model_weights(MICRO, cfg=21, w_std=0.2, diff_std=0.08)
+    W["lm_head"] = W["lm_head"] * np.float32(0.5)
+    Wt = M.Weights(W, MICRO)
+    T, N = 0.8, 6000
+    prompt = np.array([1, 5, 2, 0, 3], np.int32)
+    cache, anchor = Dc.prefill(Wt, prompt, 16)
+    p1 = sp.softmax(Dc.ar_pass(Wt, cache, [anchor])[0] / T)
+    q1 = sp.softmax(Dc.draft_pass(Wt, cache, [anchor] + [MICRO.mask_id] * 3)[0] / T)
+    joint = np.stack([p1[t] * sp.softmax(Dc.ar_pass(Wt, cache, [anchor, t])[1] / T) for t in range(8)])
+    from orthrus_round_amd.decoder import Decoder
+    dec = Decoder(W, MICRO, precision="fp32", block=4, max_batch=N, max_ctx=32)
+    prompts = np.tile(prompt, (N, 1))
+    toks, stt = dec.generate(prompts, 2, temperature=T, seed=123, poll_every=1, record_accepts=True)
+    orth = np.zeros((8, 8))
+    np.add.at(orth, (toks[:, 0], toks[:, 1]), 1)
+    acc0 = float((stt.accept_hist[0] >= 1).mean())
+    a = float(np.minimum(p1, q1).sum())
+    assert abs(acc0 - a) < 4.5 * np.sqrt(a * (1 - a) / N), (acc0, a)
+    assert _chi2_pvalue(orth.sum(1), p1) > 1e-4
+    assert _chi2_pvalue(orth, joint) > 1e-4
+    ar_toks, _ = dec.generate_ar(prompts, 2, temperature=T, seed=123)
+    ar = np.zeros((8, 8))
+    np.add.at(ar, (ar_toks[:, 0], ar_toks[:, 1]), 1)
+    assert _chi2_pvalue(ar, joint) > 1e-4
+    print(f"slot-0 accept {acc0:.3f} (law {a:.3f}); chi2 p orthrus {_chi2_pvalue(orth, joint):.3f}, "
+          f"ar {_chi2_pvalue(ar, joint):.3f}")
