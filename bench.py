@@ -25,7 +25,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--batch", type=int, default=8)
     p.add_argument("--prompt", type=int, default=4096)
     p.add_argument("--layers", type=int, default=8)
@@ -283,15 +283,47 @@ def attention_c2(replays=50):
                 fn = ((lambda: ora.draft_attn(desc, q, pk, pv, pt, cl, kb, vb, out, ws)) if name == "draft" else
                       (lambda: ora.verify_attn(desc, q, pk, pv, pt, cl, out, ws)))
                 st = alternating_ms([fn], replays, flush=True)
+                st_warm = alternating_ms([fn], replays)
                 byts = 4096 * n + (128 * 1024 if name == "draft" else 4096 * 32) + 128 * 1024 + 256 * 1024
                 flops = 4 * 16 * 128 * 32 * (n + 32)
                 row[f"{name}_chunk{chunk or 1024}"] = {
-                    "ms_stats": rounded(st, 6), "bytes": byts, "GBs_median": round(byts / st["median"] / 1e6, 1),
+                    "ms_stats": rounded(st, 6), "warm_ms_stats": rounded(st_warm, 6), "bytes": byts,
+                    "GBs_median": round(byts / st["median"] / 1e6, 1),
                     "frac_median": round(byts / st["median"] / 1e6 / HBM_PEAK_GBS, 4),
                     "mfma_frac_median": round(flops / st["median"] / 1e9 / BF16_PEAK_TFLOPS, 5)}
         res[str(n)] = row
     return {"workload": "batch 1, 16Q/8KV x 128, 32 block queries, bf16 -> fp32, cold (caches evicted before "
-                        "every call); kv_chunk 1024 (one chunk up to 1K keys) and 512 (more workgroups)", **res}
+                        "every call; warm_ms_stats: back-to-back calls, inputs cache-resident); kv_chunk 1024 (one "
+                        "chunk up to 1K keys) and 512 (more workgroups)", **res}
+
+
+def c1_tiny(n_tokens=256, reps=5):
+    """The tiny correctness decoder (2 layers, hidden 256, 4Q/2KV x 64, SwiGLU 1024, vocabulary 4096,
+    fp32, diffusion view = AR + N(0, 0.005)) on one 64-token prompt, 256 greedy tokens at block 32:
+    the whole decode (prefill excluded) with graph replay, median over reps, and the trajectory
+    against AR decoding through the same kernels."""
+    import torch
+    import synth
+    from orthrus_round_amd.decoder import Decoder
+    shape = synth.TINY
+    W = synth.model_weights(shape, cfg=1)
+    prompts = synth.prompt_ids(shape, 1, 1, 64)
+    dec = Decoder(W, shape, precision="fp32", block=32, max_batch=1, max_ctx=64 + n_tokens + 64)
+    times, toks, st = [], None, None
+    for _ in range(reps):
+        toks, st = dec.generate(prompts, n_tokens, use_graph=True, poll_every=16)
+        times.append(st.decode_s * 1e3)
+    _, sa = dec.generate(prompts, n_tokens, poll_every=1, record_accepts=True)
+    ar, _ = dec.generate_ar(prompts, n_tokens, use_graph=True)
+    accepts = [int(h[0]) for h in sa.accept_hist if int(h[0]) >= 0]
+    del dec
+    torch.cuda.empty_cache()
+    ms = float(np.median(times))
+    return {"workload": "2 layers, hidden 256, 4Q/2KV x 64, SwiGLU 1024, vocab 4096, fp32, 64-token prompt, "
+                        "256 greedy tokens, block 32, graph replay (prefill excluded)",
+            "decode_ms_median": round(ms, 3), "rounds": st.rounds, "ms_per_round": round(ms / st.rounds, 4),
+            "tokens_per_s": round(n_tokens / ms * 1e3, 1), "mean_accept": round(float(np.mean(accepts)), 3),
+            "trajectory_equals_ar": bool(np.array_equal(toks, ar))}
 
 
 def lmhead_consensus_c4(replays=50):
@@ -439,6 +471,13 @@ def cpu_baseline(W, shape, prompts_np, kv_seed=9):
     lm_s = time.perf_counter() - ta
     per["lmhead_consensus_8b_32_of_512_rows"] = {"s": round(lm_s, 3), "whole_call_s_scaled": round(16 * lm_s, 3),
                                                  "sample": "32 of the 512 rows (float64 product incl. conversion)"}
+    # the tiny correctness decoder's whole run (prefill + 256 greedy tokens), row-by-row oracle
+    Wt1 = M.Weights(synth.model_weights(synth.TINY, cfg=1), synth.TINY)
+    p1 = synth.prompt_ids(synth.TINY, 1, 1, 64)[0]
+    ta = time.perf_counter()
+    res1 = Dc.generate(Wt1, p1, 256)
+    per["c1_tiny_whole_run"] = {"s": round(time.perf_counter() - ta, 3), "rounds": len(res1.rounds),
+                                "sample": "the whole run: prefill and 256 greedy tokens"}
     return {"value": round(len(emitted) / round_s, 4), "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
             "cpu_model": cpu_model(),
             "sample": (f"float64 NumPy oracle, one whole round (draft pass, verify pass, consensus) of 1 sequence "
@@ -946,7 +985,7 @@ def main():
     ar_ms = ar_st["mean"]
     del ga
 
-    sampled = sweep = match = control = memory = two = c2 = c4 = None
+    sampled = sweep = match = control = memory = two = c1 = c2 = c4 = None
     if not args.no_extras:
         sampled = sampled_round(dec, prompts)
         print("[bench] sampled round done", file=sys.stderr, flush=True)
@@ -962,7 +1001,8 @@ def main():
     if not args.no_extras:
         c2 = attention_c2()
         c4 = lmhead_consensus_c4()
-        print("[bench] c2 / c4 legs done", file=sys.stderr, flush=True)
+        c1 = c1_tiny()
+        print("[bench] c1 / c2 / c4 legs done", file=sys.stderr, flush=True)
     attn = None if args.no_attn else attention_roofline(args.attn_chunk)
     copy_gbs = stream_copy_gbs()
     calibration_copy()
@@ -1014,6 +1054,7 @@ def main():
         "sampled_round": sampled,
         "attention_roofline": attn,
         "attention_single_layer_qwen3_1p7b": c2,
+        "tiny_decoder_c1": c1,
         "lmhead_consensus_8b": c4,
         "round_ms_by_block": sweep,
         "two_step_drafting": two,
