@@ -13,6 +13,8 @@ Parity status per function (pins live in ``tests/test_oracle_*.py``):
 * philox4x64 / uniforms ........ pinned to numpy.random.Philox words
 * rmsnorm, rope ................ pinned to torch rms_norm, complex rotation, norm/relative-position invariants
 * draft/verify attention ....... pinned to torch scaled_dot_product_attention (float64) + special cases
+* grouped_attention ............ the same attention in matrix-product form: pinned to SDPA and to the
+                                 row form
 * ar_pass / decoder rows ....... pinned to transformers' Llama decoder (float64) with the same weights
 * draft_pass ................... pinned to the same Llama with a block mask when both views share weights
 * argmax ....................... ties -> lowest id, pinned by duplicated LM-head rows
@@ -24,6 +26,9 @@ Parity status per function (pins live in ``tests/test_oracle_*.py``):
                                  greedy consensus in the T -> 0 limit
 * generate / generate_ar, T > 0  first two committed tokens follow the AR law p(t1) p(t2 | t1)
                                  (chi-square over seeded runs on a one-layer, 8-token decoder)
+* log_confidence ............... closed form on a two-logit row; exp sums to 1 over the vocabulary
+* two_step_draft ............... n_fill = 0 is the one-pass draft; the filled slots keep pass-one
+                                 tokens and are the n_fill most confident
 * generate vs generate_ar ...... losslessness (identical greedy trajectories), forced full/zero
                                  acceptance, K = 1, poisoned dead cache slots
 * token values on random weights: parity unpinned by the pages (no worked example exists);
