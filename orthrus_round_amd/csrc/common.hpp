@@ -77,6 +77,16 @@ __device__ __forceinline__ float wave_max(float v) {
   for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor_f(v, m));
   return v;
 }
+// RMSNorm workgroups (standalone and fused into the residual GEMM's reduce) have one thread per
+// 16-byte chunk of the row, rounded up to whole waves, at most kNormMaxChunks; longer rows use
+// kNormMaxChunks threads and a strided loop.
+constexpr int kNormMaxChunks = 1024;
+inline int norm_threads(int n, int elem_bytes) {
+  const int chunks = (int)(((int64_t)n * elem_bytes + 15) / 16);
+  const int t = ((chunks + 63) / 64) * 64;
+  return t < 64 ? 64 : (t > kNormMaxChunks ? kNormMaxChunks : t);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_f(v, m);

@@ -25,43 +25,37 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ embed,
 }
 
 // -------------------------------------------------------------------------------------- rmsnorm
-// One workgroup per row.  Rows whose length is a multiple of 16 bytes and at most NCH chunks per
-// thread are read once, with 16-byte loads kept in registers; the sum of squares is reduced in a
-// fixed order (per thread in chunk order, then a wave butterfly, then the four waves in order).
+// One workgroup per row.  Rows whose length is a multiple of 16 bytes and at most
+// kNormMaxChunks 16-byte chunks take the register path: thread c owns chunk c (one 16-byte load,
+// issued with every other load of the row at once), and the sum of squares is reduced in a fixed
+// order: per thread in element order, a wave butterfly, then the waves in order.  The workgroup
+// has one thread per chunk, rounded up to whole waves.  Other rows take a strided loop.
 template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const T* __restrict__ x, const float* __restrict__ g, float eps,
-                                                      int hidden, T* __restrict__ y, int aligned16) {
+__global__ __launch_bounds__(kNormMaxChunks) void rmsnorm_kernel(const T* __restrict__ x, const float* __restrict__ g,
+                                                                 float eps, int hidden, T* __restrict__ y,
+                                                                 int aligned16) {
   constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
-  constexpr int NCH = 4;               // chunks per thread held in registers
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-  __shared__ float red[4];
-  const int m = blockIdx.x, tid = threadIdx.x;
+  __shared__ float red[kNormMaxChunks / 64];
+  const int m = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
   const T* xr = x + (size_t)m * hidden;
   T* yr = y + (size_t)m * hidden;
   const int nch = hidden / EPC;
-  const bool vec = aligned16 && hidden % EPC == 0 && nch <= NCH * 256;
+  const bool vec = aligned16 && hidden % EPC == 0 && nch <= nt;
   float ss = 0.0f;
-  u32x4_t buf[NCH];
+  u32x4_t buf = {0, 0, 0, 0};
   if (vec) {
+    if (tid < nch) {
+      buf = *reinterpret_cast<const u32x4_t*>(xr + (size_t)tid * EPC);
+      const T* e = reinterpret_cast<const T*>(&buf);
 #pragma unroll
-    for (int q = 0; q < NCH; ++q) {
-      const int c = q * 256 + tid;
-      if (c < nch) buf[q] = *reinterpret_cast<const u32x4_t*>(xr + (size_t)c * EPC);
-    }
-#pragma unroll
-    for (int q = 0; q < NCH; ++q) {
-      const int c = q * 256 + tid;
-      if (c < nch) {
-        const T* e = reinterpret_cast<const T*>(&buf[q]);
-#pragma unroll
-        for (int i = 0; i < EPC; ++i) {
-          const float v = to_f32(e[i]);
-          ss += v * v;
-        }
+      for (int i = 0; i < EPC; ++i) {
+        const float v = to_f32(e[i]);
+        ss += v * v;
       }
     }
   } else {
-    for (int i = tid; i < hidden; i += 256) {
+    for (int i = tid; i < hidden; i += nt) {
       const float v = to_f32(xr[i]);
       ss += v * v;
     }
@@ -69,23 +63,20 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* __restrict__ x, c
   ss = wave_sum(ss);
   if ((tid & 63) == 0) red[tid >> 6] = ss;
   __syncthreads();
-  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  float tot = 0.0f;
+  for (int w = 0; w < nt / 64; ++w) tot += red[w];
   const float inv = 1.0f / sqrtf(tot / (float)hidden + eps);
   if (vec) {
+    if (tid < nch) {
+      const T* e = reinterpret_cast<const T*>(&buf);
+      u32x4_t o;
+      T* oe = reinterpret_cast<T*>(&o);
 #pragma unroll
-    for (int q = 0; q < NCH; ++q) {
-      const int c = q * 256 + tid;
-      if (c < nch) {
-        const T* e = reinterpret_cast<const T*>(&buf[q]);
-        u32x4_t o;
-        T* oe = reinterpret_cast<T*>(&o);
-#pragma unroll
-        for (int i = 0; i < EPC; ++i) oe[i] = from_f32<T>(to_f32(e[i]) * inv * g[(size_t)c * EPC + i]);
-        *reinterpret_cast<u32x4_t*>(yr + (size_t)c * EPC) = o;
-      }
+      for (int i = 0; i < EPC; ++i) oe[i] = from_f32<T>(to_f32(e[i]) * inv * g[(size_t)tid * EPC + i]);
+      *reinterpret_cast<u32x4_t*>(yr + (size_t)tid * EPC) = o;
     }
   } else {
-    for (int i = tid; i < hidden; i += 256) yr[i] = from_f32<T>(to_f32(xr[i]) * inv * g[i]);
+    for (int i = tid; i < hidden; i += nt) yr[i] = from_f32<T>(to_f32(xr[i]) * inv * g[i]);
   }
 }
 
@@ -184,11 +175,12 @@ extern "C" int32_t orthrus_rmsnorm(int32_t rows, int32_t hidden, int32_t dtype, 
   if (rows == 0) return ORTHRUS_OK;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int aligned16 = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15) == 0;
+  const int nt = norm_threads(hidden, dtype_size(dtype));
   if (dtype == ORTHRUS_BF16)
-    hipLaunchKernelGGL(rmsnorm_kernel<bf16>, dim3(rows), dim3(256), 0, st, (const bf16*)x, gain, eps, hidden, (bf16*)y,
+    hipLaunchKernelGGL(rmsnorm_kernel<bf16>, dim3(rows), dim3(nt), 0, st, (const bf16*)x, gain, eps, hidden, (bf16*)y,
                        aligned16);
   else
-    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(rows), dim3(256), 0, st, (const float*)x, gain, eps, hidden,
+    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(rows), dim3(nt), 0, st, (const float*)x, gain, eps, hidden,
                        (float*)y, aligned16);
   return check_launch("orthrus_rmsnorm");
 }

@@ -159,78 +159,65 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restric
 }
 
 // The residual k-slice reduce fused with the RMSNorm that follows every residual GEMM of a layer:
-// x = x + (((P0 + P1) + P2) + ...) (stored), then y = rmsnorm(x) * g.  One workgroup per row.  Each thread
-// owns the same 16-byte chunks of the row as rmsnorm_kernel (chunk c = q * 256 + tid) and the sum of
-// squares runs over the stored (rounded) x in the same order (per thread in chunk order, a wave
-// butterfly, then the four waves in order), so the result has the bits of the residual GEMM
-// followed by orthrus_rmsnorm.
+// x = x + (((P0 + P1) + P2) + ...) (stored), then y = rmsnorm(x) * g.  One workgroup per row with
+// rmsnorm_kernel's shape: thread c owns 16-byte chunk c of the row, and issues its residual load and
+// all S partial loads at once (one memory round trip); the sum of squares runs over the stored
+// (rounded) x in rmsnorm_kernel's order (per thread in element order, a wave butterfly, then the
+// waves in order), so the result has the bits of the residual GEMM followed by orthrus_rmsnorm.
 template <typename T, int S>
-__global__ __launch_bounds__(256) void gemm_reduce_rmsnorm_kernel(const float* __restrict__ P, T* x,
-                                                                  const float* __restrict__ g, float eps, int M,
-                                                                  int N, T* __restrict__ y) {
-  constexpr int EPC = 16 / sizeof(T), NCH = 4;
+__global__ __launch_bounds__(kNormMaxChunks) void gemm_reduce_rmsnorm_kernel(const float* __restrict__ P, T* x,
+                                                                             const float* __restrict__ g, float eps,
+                                                                             int M, int N, T* __restrict__ y) {
+  constexpr int EPC = 16 / sizeof(T), NV = EPC / 4;  // elements and float4 partial loads per chunk
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-  __shared__ float red[4];
-  const int m = blockIdx.x, tid = threadIdx.x;
+  __shared__ float red[kNormMaxChunks / 64];
+  const int m = blockIdx.x, c = threadIdx.x, nt = blockDim.x;
   const size_t MN = (size_t)M * N;
   T* xr = x + (size_t)m * N;
   T* yr = y + (size_t)m * N;
   const float* pr = P + (size_t)m * N;
-  const int nch = N / EPC;
-  u32x4_t buf[NCH];
-#pragma unroll
-  for (int q = 0; q < NCH; ++q) {
-    const int c = q * 256 + tid;
-    if (c < nch) {
-      const u32x4_t rv = *reinterpret_cast<const u32x4_t*>(xr + (size_t)c * EPC);
-      const T* re = reinterpret_cast<const T*>(&rv);
-      T* xe = reinterpret_cast<T*>(&buf[q]);
-#pragma unroll
-      for (int i = 0; i < EPC; i += 4) {
-        const size_t o = (size_t)c * EPC + i;
-        f32x4 pp[S];
-#pragma unroll
-        for (int k = 0; k < S; ++k) pp[k] = *reinterpret_cast<const f32x4*>(pr + o + k * MN);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          float sum = pp[0][v];
-#pragma unroll
-          for (int k = 1; k < S; ++k) sum += pp[k][v];
-          xe[i + v] = from_f32<T>(to_f32(re[i + v]) + sum);
-        }
-      }
-      *reinterpret_cast<u32x4_t*>(xr + (size_t)c * EPC) = buf[q];
-    }
-  }
+  const bool own = c < N / EPC;
+  u32x4_t buf = {0, 0, 0, 0};
   float ss = 0.0f;
+  if (own) {
+    const size_t o = (size_t)c * EPC;
+    f32x4 pp[S][NV];
 #pragma unroll
-  for (int q = 0; q < NCH; ++q) {
-    const int c = q * 256 + tid;
-    if (c < nch) {
-      const T* e = reinterpret_cast<const T*>(&buf[q]);
+    for (int k = 0; k < S; ++k)
 #pragma unroll
-      for (int i = 0; i < EPC; ++i) {
-        const float v = to_f32(e[i]);
-        ss += v * v;
+      for (int j = 0; j < NV; ++j) pp[k][j] = *reinterpret_cast<const f32x4*>(pr + o + 4 * j + k * MN);
+    const u32x4_t rv = *reinterpret_cast<const u32x4_t*>(xr + o);
+    const T* re = reinterpret_cast<const T*>(&rv);
+    T* xe = reinterpret_cast<T*>(&buf);
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float sum = pp[0][j][v];
+#pragma unroll
+        for (int k = 1; k < S; ++k) sum += pp[k][j][v];
+        xe[4 * j + v] = from_f32<T>(to_f32(re[4 * j + v]) + sum);
       }
+    *reinterpret_cast<u32x4_t*>(xr + o) = buf;
+#pragma unroll
+    for (int i = 0; i < EPC; ++i) {
+      const float v = to_f32(xe[i]);
+      ss += v * v;
     }
   }
   ss = wave_sum(ss);
-  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  if ((c & 63) == 0) red[c >> 6] = ss;
   __syncthreads();
-  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  float tot = 0.0f;
+  for (int w = 0; w < nt / 64; ++w) tot += red[w];
   const float inv = 1.0f / sqrtf(tot / (float)N + eps);
+  if (own) {
+    const T* e = reinterpret_cast<const T*>(&buf);
+    u32x4_t o;
+    T* oe = reinterpret_cast<T*>(&o);
 #pragma unroll
-  for (int q = 0; q < NCH; ++q) {
-    const int c = q * 256 + tid;
-    if (c < nch) {
-      const T* e = reinterpret_cast<const T*>(&buf[q]);
-      u32x4_t o;
-      T* oe = reinterpret_cast<T*>(&o);
-#pragma unroll
-      for (int i = 0; i < EPC; ++i) oe[i] = from_f32<T>(to_f32(e[i]) * inv * g[(size_t)c * EPC + i]);
-      *reinterpret_cast<u32x4_t*>(yr + (size_t)c * EPC) = o;
-    }
+    for (int i = 0; i < EPC; ++i) oe[i] = from_f32<T>(to_f32(e[i]) * inv * g[(size_t)c * EPC + i]);
+    *reinterpret_cast<u32x4_t*>(yr + (size_t)c * EPC) = o;
   }
 }
 
@@ -452,7 +439,7 @@ int32_t launch(int M, int N, int K, int epi, const void* a, const void* w, const
 template <typename T>
 bool fused_norm_ok(int N, int K, int dtype, const void* x, const void* y) {
   constexpr int EPC = 16 / (int)sizeof(T);
-  return k_splits(N, K, dtype) && N % EPC == 0 && N / EPC <= 4 * 256 &&
+  return k_splits(N, K, dtype) && N % EPC == 0 && N / EPC <= kNormMaxChunks &&
          ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15) == 0;
 }
 
@@ -460,11 +447,12 @@ template <typename T>
 int32_t launch_residual_rmsnorm(int M, int N, int K, const void* a, const void* w, void* x, const float* gain,
                                 float eps, void* y, float* P, hipStream_t st) {
   const int S = launch_quarter_tiles<T>(M, N, K, a, w, P, st);
+  const int nt = norm_threads(N, (int)sizeof(T));  // one thread per 16-byte chunk, as rmsnorm_kernel
   if (S == 8)
-    hipLaunchKernelGGL((gemm_reduce_rmsnorm_kernel<T, 8>), dim3(M), dim3(256), 0, st, P, reinterpret_cast<T*>(x), gain,
+    hipLaunchKernelGGL((gemm_reduce_rmsnorm_kernel<T, 8>), dim3(M), dim3(nt), 0, st, P, reinterpret_cast<T*>(x), gain,
                        eps, M, N, reinterpret_cast<T*>(y));
   else
-    hipLaunchKernelGGL((gemm_reduce_rmsnorm_kernel<T, 4>), dim3(M), dim3(256), 0, st, P, reinterpret_cast<T*>(x), gain,
+    hipLaunchKernelGGL((gemm_reduce_rmsnorm_kernel<T, 4>), dim3(M), dim3(nt), 0, st, P, reinterpret_cast<T*>(x), gain,
                        eps, M, N, reinterpret_cast<T*>(y));
   return check_launch("orthrus_gemm_residual_rmsnorm");
 }
