@@ -310,6 +310,10 @@ template <typename T> using PlainMid = GemmCfg<T, 64, 128, 2, 2, 3, 3>;
 template <typename T> using PlainBig = GemmCfg<T, 128, 128, 2, 2, ORTHRUS_PB_RINGS>;
 // 128 x 192 tiles of eight 32 x 96 wavefronts, one workgroup per CU (128 KiB of LDS)
 template <typename T> using Plain192 = GemmCfg<T, 128, 192, 4, 2, 2, 4>;
+// 128 x 128 tiles of eight 32 x 64 wavefronts (80 KiB of rings) for the four-slice N = 4096 case (the
+// O projection: 256 workgroups, one per CU): twice the wavefronts of PlainBig per tile to hide the
+// short main loop's latency (27.6 -> 24.1 us per launch with its reduce at M = 256, same bits)
+template <typename T> using Plain128w8 = GemmCfg<T, 128, 128, 4, 2, 2, 3>;
 // Above 128 rows the wide family runs 128 x 192 tiles of eight 32 x 96 wavefronts (two per SIMD
 // at one workgroup per CU).  At M = 256 the 24576-wide gate/up projection is then 2 x 128 = 256
 // tiles, one per CU (256 x 128 tiles left 64 CUs idle), and each workgroup streams 2.5 MiB of
@@ -380,8 +384,10 @@ int launch_quarter_tiles(int M, int N, int K, const void* a, const void* w, floa
   if (M <= 32) launch_quarter_cfg<T, PlainSmall<T>>(M, N, K, S, a, w, P, st);
   else if (M <= 64) launch_quarter_cfg<T, PlainMid<T>>(M, N, K, S, a, w, P, st);
   // q/k/v (N = 6144) at M = 256: 2 x 32 x 4 = 256 workgroups of 128 x 192 instead of 384 of 128 x 128
-  // (31.7 -> 27.3-27.9 us back to back); O and down (N = 4096) keep 128 x 128
+  // (31.7 -> 27.3-27.9 us back to back); O and down (N = 4096) keep 128 x 128 tiles, with eight
+  // wavefronts when there are four slices (one workgroup per CU) and four when there are eight
   else if (N % 192 == 0) launch_quarter_cfg<T, Plain192<T>>(M, N, K, S, a, w, P, st);
+  else if (S == 4) launch_quarter_cfg<T, Plain128w8<T>>(M, N, K, S, a, w, P, st);
   else launch_quarter_cfg<T, PlainBig<T>>(M, N, K, S, a, w, P, st);
   return S;
 }
