@@ -143,8 +143,12 @@ def kernel_table(dec, ctx_np, sweeps=50):
     add("gemm_o_residual_rmsnorm", lambda i: L.gemm_residual_rmsnorm(M, H, Hq * D, dt, dec.o, Ly[i]["o_ar"], dec.x,
                                                                      Ly[i]["mlp_norm"], s.eps, dec.a, dec.gemm_ws),
         2 * s.layers, (H * Hq * D + M * Hq * D + 3 * M * H) * esz, 2 * M * H * Hq * D)
-    add("gemm_gate_up_swiglu", lambda i: L.gemm(M, 2 * I, H, dt, dt, L.EPI_SWIGLU, dec.a, Ly[i]["gate_up"], None, dec.h, dec.gemm_ws),
-        2 * s.layers, (2 * I * H + M * H + M * I) * esz, 2 * M * 2 * I * H)
+    def gate_up(i):  # the path the decoder takes at these rows
+        if Ly[i]["gate_up_frag"] is not None and M > 64:
+            L.gemm_swiglu_fragments(M, I, H, dt, dec.a, Ly[i]["gate_up_frag"], dec.h)
+        else:
+            L.gemm(M, 2 * I, H, dt, dt, L.EPI_SWIGLU, dec.a, Ly[i]["gate_up"], None, dec.h, dec.gemm_ws)
+    add("gemm_gate_up_swiglu", gate_up, 2 * s.layers, (2 * I * H + M * H + M * I) * esz, 2 * M * 2 * I * H)
     add("gemm_down_residual_rmsnorm", lambda i: L.gemm_residual_rmsnorm(M, H, I, dt, dec.h, Ly[i]["down"], dec.x,
                                                                         Ly[i]["attn_norm"], s.eps, dec.a, dec.gemm_ws),
         2 * s.layers, (H * I + M * I + 3 * M * H) * esz, 2 * M * H * I)
@@ -167,7 +171,7 @@ def kernel_table(dec, ctx_np, sweeps=50):
 
 # The sources each timed kernel is compiled from (orthrus_round_amd/csrc/).
 KERNEL_SOURCES = {
-    "gemm": ("gemm.hip", "gemm_core.hpp", "common.hpp"),
+    "gemm": ("gemm.hip", "gemm_core.hpp", "gemm_rs.hpp", "common.hpp"),
     "attn": ("attn.hip", "common.hpp"),
     "lmhead": ("lmhead.hip", "gemm_core.hpp", "common.hpp"),
     "rmsnorm": ("elementwise.hip", "common.hpp"),
@@ -811,7 +815,7 @@ def summarize_counters(fetch_dir, write_dir, out_json):
     parts = {
         "gemm_qkv_rope_kv": ["gemm_quarter_kernel", "gemm_reduce_rope_kv_kernel"],
         "gemm_o_residual_rmsnorm": ["gemm_quarter_kernel", "gemm_reduce_rmsnorm_kernel"],
-        "gemm_gate_up_swiglu": ["gemm_kernel"],
+        "gemm_gate_up_swiglu": ["gemm_kernel", "rs_swiglu_kernel"],
         "gemm_down_residual_rmsnorm": ["gemm_quarter_kernel", "gemm_reduce_rmsnorm_kernel"],
         "attn_draft": ["attn_kernel", "attn_combine_kernel"],
         "attn_verify": ["attn_kernel", "attn_combine_kernel"],
@@ -840,7 +844,7 @@ def summarize_counters(fetch_dir, write_dir, out_json):
                     name = "gemm_down_residual_rmsnorm"
                 order.append((name, [seq[i], seq[i + 1]]))
                 i += 2
-            elif "gemm_kernel" in k:
+            elif "gemm_kernel" in k or "rs_swiglu_kernel" in k:
                 order.append(("gemm_gate_up_swiglu", [seq[i]]))
                 i += 1
             elif "attn_kernel" in k:

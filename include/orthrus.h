@@ -256,6 +256,21 @@ int32_t orthrus_gemm_residual_rmsnorm(int32_t M, int32_t N, int32_t K, int32_t d
 int32_t orthrus_pack_gate_up(int32_t inter, int32_t hidden, int32_t dtype, const void* gate,
                              const void* up, void* packed, void* stream);
 
+/* The gate/up + SwiGLU GEMM on fragment-packed weights, for rows that are many (the round's 32
+ * rows per sequence).  orthrus_pack_gate_up_fragments writes gate [I, H] and up [I, H], interleaved
+ * in 32-row groups as orthrus_pack_gate_up does, in an MFMA-fragment order (4 KiB pieces, one
+ * per 64-wide k stage and 32-row block, stage-major; 2 * I * H elements, the same size as the
+ * row-interleaved packing), from which each wavefront loads its weight fragments straight into
+ * registers.  orthrus_gemm_swiglu_fragments then computes c [M, I] = silu(a w_gate^T) * (a w_up^T)
+ * with a [M, H], fp32 accumulation in the one-loop k order, so c has exactly the bits of
+ * orthrus_gemm(M, 2I, H, dtype, dtype, ORTHRUS_EPI_SWIGLU, a, w) on the row-interleaved packing.
+ * Built for bf16 with H = 4096 and 2I a multiple of 256 and >= 16384; other shapes return
+ * ORTHRUS_ERR_UNSUPPORTED (use orthrus_gemm).  Pointers 16-byte aligned; no workspace. */
+int32_t orthrus_pack_gate_up_fragments(int32_t inter, int32_t hidden, int32_t dtype,
+                                       const void* gate, const void* up, void* packed, void* stream);
+int32_t orthrus_gemm_swiglu_fragments(int32_t M, int32_t inter, int32_t hidden, int32_t dtype,
+                                      const void* a, const void* w_fragments, void* c, void* stream);
+
 /* y [rows, hidden] = x / sqrt(mean(x^2) + eps) * gain, fp32 math; x and y in `dtype`. */
 int32_t orthrus_rmsnorm(int32_t rows, int32_t hidden, int32_t dtype, const void* x,
                         const float* gain, float eps, void* y, void* stream);

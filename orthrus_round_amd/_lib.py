@@ -65,6 +65,8 @@ _SIGS = {
                                     _P, _P, _P, _P, _P, _P, _SZ, _P], _I32),
     "orthrus_gemm_residual_rmsnorm": ([_I32, _I32, _I32, _I32, _P, _P, _P, _P, _F32, _P, _P, _SZ, _P], _I32),
     "orthrus_pack_gate_up": ([_I32, _I32, _I32, _P, _P, _P, _P], _I32),
+    "orthrus_pack_gate_up_fragments": ([_I32, _I32, _I32, _P, _P, _P, _P], _I32),
+    "orthrus_gemm_swiglu_fragments": ([_I32, _I32, _I32, _I32, _P, _P, _P, _P], _I32),
     "orthrus_rmsnorm": ([_I32, _I32, _I32, _P, _P, _F32, _P, _P], _I32),
     "orthrus_rope_table": ([_I32, _I32, ctypes.c_double, _P, _P], _I32),
     "orthrus_rope_kv_write": ([_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _I32, _P, _P, _P, _P,
@@ -218,6 +220,16 @@ def gemm_rope_kv_write(batch, block, q_heads, kv_heads, head_dim, page_size, max
 
 def pack_gate_up(inter, hidden, dtype, gate, up, packed, stream=None):
     _check(lib().orthrus_pack_gate_up(inter, hidden, dtype, _ptr(gate), _ptr(up), _ptr(packed), _stream(stream)))
+
+
+def pack_gate_up_fragments(inter, hidden, dtype, gate, up, packed, stream=None):
+    _check(lib().orthrus_pack_gate_up_fragments(inter, hidden, dtype, _ptr(gate), _ptr(up), _ptr(packed),
+                                                _stream(stream)))
+
+
+def gemm_swiglu_fragments(M, inter, hidden, dtype, a, w_fragments, c, stream=None):
+    _check(lib().orthrus_gemm_swiglu_fragments(M, inter, hidden, dtype, _ptr(a), _ptr(w_fragments), _ptr(c),
+                                               _stream(stream)))
 
 
 def rmsnorm(rows, hidden, dtype, x, gain, eps, y, stream=None):

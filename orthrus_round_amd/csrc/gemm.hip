@@ -7,6 +7,7 @@
 // tiles, which stream half the operand bytes of 64x64 tiles through L2.  Wide outputs (gate/up)
 // use plain tiles over the whole K.  Either way an output element's summation order depends on
 // (N, K) only, so results are deterministic and a row's bits do not depend on the batch size.
+#include "gemm_rs.hpp"
 #include "gemm_core.hpp"
 
 namespace orthrus {
@@ -426,6 +427,63 @@ int32_t launch_quarters(int M, int N, int K, int epi, const void* a, const void*
   return check_launch("orthrus_gemm");
 }
 
+
+// -------------------------------------------------------------------- fragment-packed gate/up
+// The gate/up + SwiGLU GEMM on fragment-packed weights (gemm_rs.hpp): same k order as the one-loop
+// family (N >= 16384), so the same bits as gemm_kernel with ORTHRUS_EPI_SWIGLU on the row-interleaved
+// packing.  Workgroup tile 128 x 256 (four wavefronts of 128 x 64: two gate/up column-block pairs).
+constexpr int kRsStages = 64;  // K = 64 * 64 = 4096, the instantiated width
+using RsSwiglu = RsCfg<4, 2, 4, 2, 4>;
+
+template <typename Cfg>
+__global__ __launch_bounds__(Cfg::NT) void rs_swiglu_kernel(const bf16* __restrict__ A, const bf16* __restrict__ Wp,
+                                                            bf16* __restrict__ C, int M, int N, int K) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int mtiles = (M + Cfg::BM - 1) / Cfg::BM;
+  int sp, mt, nt;
+  xcd_tile_map(blockIdx.x, gridDim.x, 1, mtiles, sp, mt, nt);
+  const int m0 = mt * Cfg::BM, n0 = nt * Cfg::BN;
+  f32x16 acc[Cfg::TMW][Cfg::TNW];
+  rs_mainloop<Cfg, kRsStages>(A, Wp, M, N, K, m0, n0, 0, smem, acc);
+  const int lane = threadIdx.x & 63, hh = lane >> 5, r = lane & 31, wu = threadIdx.x >> 6;
+  const int NO = N / 2;
+  static_assert(Cfg::TNW % 2 == 0, "gate/up column-block pairs");
+#pragma unroll
+  for (int jp = 0; jp < Cfg::TNW; jp += 2) {
+    const int ng = n0 + (wu * Cfg::TNW + jp) * 32;  // the pair's gate block; the up block follows
+    if (ng >= N) continue;
+    const int col = ng / 2 + r;
+#pragma unroll
+    for (int i = 0; i < Cfg::TMW; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + i * 32 + acc_row(e, hh);
+        if (m < M) {
+          const float g = acc[i][jp][e], u = acc[i][jp + 1][e];
+          const float sg = g / (1.0f + expf(-g));
+          C[(size_t)m * NO + col] = from_f32<bf16>(sg * u);
+        }
+      }
+  }
+}
+
+// gate/up rows interleaved in 32-row groups (as pack_gate_up_kernel) and written in the
+// fragment-packed layout, one 8-element chunk per thread
+__global__ void pack_gate_up_fragments_kernel(const bf16* __restrict__ g, const bf16* __restrict__ u,
+                                              bf16* __restrict__ p, int inter, int hidden) {
+  const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const int N = 2 * inter, K = hidden;
+  if (t >= (size_t)N * (K / 8)) return;
+  const int n = (int)(t / (K / 8)), k = (int)(t % (K / 8)) * 8;
+  const int grp = n / 64, within = n % 64;
+  const bf16* src = (within < 32 ? g : u) + (size_t)(grp * 32 + (within & 31)) * K + k;
+  *reinterpret_cast<bf16x8*>(p + packed_offset(n, k, N, K)) = *reinterpret_cast<const bf16x8*>(src);
+}
+
+bool rs_swiglu_ok(int inter, int hidden, int dtype) {
+  return dtype == ORTHRUS_BF16 && hidden == 64 * kRsStages && 2 * inter >= kWideN && (2 * inter) % RsSwiglu::BN == 0;
+}
+
 template <typename T, typename OutT>
 int32_t launch(int M, int N, int K, int epi, const void* a, const void* w, const void* res, void* c, float* P,
                hipStream_t st) {
@@ -601,4 +659,40 @@ extern "C" int32_t orthrus_pack_gate_up(int32_t inter, int32_t hidden, int32_t d
     hipLaunchKernelGGL(pack_gate_up_kernel<float>, dim3(2 * inter), dim3(256), 0, st, (const float*)gate,
                        (const float*)up, (float*)packed, inter, hidden);
   return check_launch("orthrus_pack_gate_up");
+}
+
+extern "C" int32_t orthrus_pack_gate_up_fragments(int32_t inter, int32_t hidden, int32_t dtype, const void* gate,
+                                                  const void* up, void* packed, void* stream) {
+  ORTHRUS_REQUIRE(inter > 0 && hidden > 0 && gate && up && packed, ORTHRUS_ERR_INVALID_ARG,
+                  "pack_gate_up_fragments: bad args");
+  ORTHRUS_REQUIRE(rs_swiglu_ok(inter, hidden, dtype), ORTHRUS_ERR_UNSUPPORTED,
+                  "pack_gate_up_fragments: built for bf16, hidden %d and 2*inter a multiple of %d >= %d "
+                  "(got dtype %d, hidden %d, inter %d)", 64 * kRsStages, RsSwiglu::BN, kWideN, dtype, hidden, inter);
+  ORTHRUS_REQUIRE(((reinterpret_cast<uintptr_t>(gate) | reinterpret_cast<uintptr_t>(up) |
+                    reinterpret_cast<uintptr_t>(packed)) & 15) == 0, ORTHRUS_ERR_INVALID_ARG,
+                  "pack_gate_up_fragments: pointers must be 16-byte aligned");
+  const size_t n = (size_t)2 * inter * (hidden / 8);
+  hipLaunchKernelGGL(pack_gate_up_fragments_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), (const bf16*)gate, (const bf16*)up, (bf16*)packed, inter,
+                     hidden);
+  return check_launch("orthrus_pack_gate_up_fragments");
+}
+
+extern "C" int32_t orthrus_gemm_swiglu_fragments(int32_t M, int32_t inter, int32_t hidden, int32_t dtype,
+                                                 const void* a, const void* w_fragments, void* c, void* stream) {
+  ORTHRUS_REQUIRE(M >= 0 && inter > 0 && hidden > 0, ORTHRUS_ERR_INVALID_ARG, "gemm_swiglu_fragments: bad sizes");
+  ORTHRUS_REQUIRE(rs_swiglu_ok(inter, hidden, dtype), ORTHRUS_ERR_UNSUPPORTED,
+                  "gemm_swiglu_fragments: built for bf16, hidden %d and 2*inter a multiple of %d >= %d",
+                  64 * kRsStages, RsSwiglu::BN, kWideN);
+  ORTHRUS_REQUIRE(a && w_fragments && c, ORTHRUS_ERR_INVALID_ARG, "gemm_swiglu_fragments: null pointer");
+  ORTHRUS_REQUIRE(((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(w_fragments)) & 15) == 0,
+                  ORTHRUS_ERR_INVALID_ARG, "gemm_swiglu_fragments: a and w must be 16-byte aligned");
+  if (M == 0) return ORTHRUS_OK;
+  const int N = 2 * inter;
+  const int mtiles = (M + RsSwiglu::BM - 1) / RsSwiglu::BM, ntiles = N / RsSwiglu::BN;
+  allow_lds(rs_swiglu_kernel<RsSwiglu>, RsSwiglu::RING);
+  hipLaunchKernelGGL(rs_swiglu_kernel<RsSwiglu>, dim3(mtiles * ntiles), dim3(RsSwiglu::NT), RsSwiglu::RING,
+                     reinterpret_cast<hipStream_t>(stream), reinterpret_cast<const bf16*>(a),
+                     reinterpret_cast<const bf16*>(w_fragments), reinterpret_cast<bf16*>(c), M, N, hidden);
+  return check_launch("orthrus_gemm_swiglu_fragments");
 }

@@ -77,10 +77,22 @@ class Decoder:
         self.lm_head = up(W["lm_head"])
         self.final_norm = up(W["final_norm"], torch.float32)
         self.layers = []
+        # gate/up: the row-interleaved packing for every row count, and where the library builds it,
+        # the fragment-packed copy that the register-streamed kernel reads for more than 64 rows
+        self.frag_gate_up = True
         for l in range(s.layers):
             gate, upw = up(W[f"{l}.w_gate"]), up(W[f"{l}.w_up"])
             gu = torch.empty((2 * I, H), dtype=self.tdt, device=self.dev)
             L.pack_gate_up(I, H, self.dt, gate, upw, gu)
+            gu_frag = None
+            if self.frag_gate_up:
+                gu_frag = torch.empty((2 * I, H), dtype=self.tdt, device=self.dev)
+                try:
+                    L.pack_gate_up_fragments(I, H, self.dt, gate, upw, gu_frag)
+                except L.OrthrusError as e:
+                    if e.status != 2:  # anything but "shape not built" is a real error
+                        raise
+                    gu_frag, self.frag_gate_up = None, False
             del gate, upw
             self.layers.append(dict(
                 attn_norm=up(W[f"{l}.attn_norm"], torch.float32),
@@ -90,6 +102,7 @@ class Decoder:
                 qkv_diff=up(np.concatenate([W[f"{l}.dq"], W[f"{l}.dk"], W[f"{l}.dv"]])),
                 o_diff=up(W[f"{l}.do"]),
                 gate_up=gu,
+                gate_up_frag=gu_frag,
                 down=up(W[f"{l}.w_down"]),
             ))
         torch.cuda.synchronize(self.dev)
@@ -180,7 +193,10 @@ class Decoder:
                 L.verify_attn(desc, self.q, self.k_pages[l], self.v_pages[l], self.page_table, ctx, self.o, ws)
             L.gemm_residual_rmsnorm(M, H, Hq * D, dt, self.o, Wl["o_" + view], x, Wl["mlp_norm"], s.eps, a,
                                     self.gemm_ws)
-            L.gemm(M, 2 * I, H, dt, dt, L.EPI_SWIGLU, a, Wl["gate_up"], None, self.h, self.gemm_ws)
+            if Wl["gate_up_frag"] is not None and M > 64:
+                L.gemm_swiglu_fragments(M, I, H, dt, a, Wl["gate_up_frag"], self.h)
+            else:
+                L.gemm(M, 2 * I, H, dt, dt, L.EPI_SWIGLU, a, Wl["gate_up"], None, self.h, self.gemm_ws)
             L.gemm_residual_rmsnorm(M, H, I, dt, self.h, Wl["down"], x, nxt, s.eps, a, self.gemm_ws)
 
     def _lm_head(self, nb, kb, tokens, temperature=0.0, seed=0, stream_id=L.STREAM_DRAFT, logits=None, lse=None,
@@ -222,6 +238,8 @@ class Decoder:
             view["ar"] += nb(ly["qkv_ar"]) + nb(ly["o_ar"])
             view["diff"] += nb(ly["qkv_diff"]) + nb(ly["o_diff"])
             shared += nb(ly["attn_norm"]) + nb(ly["mlp_norm"]) + nb(ly["gate_up"]) + nb(ly["down"])
+            if ly["gate_up_frag"] is not None:
+                shared += nb(ly["gate_up_frag"])
         kv = sum(nb(t) for t in self.k_pages) + sum(nb(t) for t in self.v_pages)
         blk = nb(self.k_blk) + nb(self.v_blk)
         attn_ws = sum(nb(t) for t in self.attn_ws.values())
