@@ -166,15 +166,12 @@ inline bool valid_dtype(int32_t dt) { return dt == ORTHRUS_BF16 || dt == ORTHRUS
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Kernels that take more than 64 KiB of dynamic LDS must opt in once per instantiation.
+// Kernels that take more than 64 KiB of dynamic LDS opt in, once per kernel.  Kernels of one
+// signature share a pointer type, so the kernels already done are kept by address.
+void allow_lds_once(const void* kernel, size_t bytes);
 template <typename K>
 inline void allow_lds(K kernel, size_t bytes) {
-  static bool done = false;
-  if (!done && bytes > 65536) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)bytes);
-    done = true;
-  }
+  if (bytes > 65536) allow_lds_once(reinterpret_cast<const void*>(kernel), bytes);
 }
 
 }  // namespace orthrus

@@ -434,6 +434,12 @@ int32_t launch_quarters(int M, int N, int K, int epi, const void* a, const void*
 // packing.  Workgroup tile 128 x 256 (four wavefronts of 128 x 64: two gate/up column-block pairs).
 constexpr int kRsStages = 64;  // K = 64 * 64 = 4096, the instantiated width
 using RsSwiglu = RsCfg<4, 2, 4, 2, 4>;
+// 128x192 tiles of six 128x32 wavefronts: 256 workgroups at M = 256 and N = 24576 (every CU busy,
+// against 192 with 128x256 tiles), 2.5 MiB of operands per workgroup instead of 3.
+#ifndef ORTHRUS_RS192_NB
+#define ORTHRUS_RS192_NB 6
+#endif
+using RsSwiglu192 = RsCfg<4, 1, 6, 2, ORTHRUS_RS192_NB>;
 
 template <typename Cfg>
 __global__ __launch_bounds__(Cfg::NT) void rs_swiglu_kernel(const bf16* __restrict__ A, const bf16* __restrict__ Wp,
@@ -447,23 +453,52 @@ __global__ __launch_bounds__(Cfg::NT) void rs_swiglu_kernel(const bf16* __restri
   rs_mainloop<Cfg, kRsStages>(A, Wp, M, N, K, m0, n0, 0, smem, acc);
   const int lane = threadIdx.x & 63, hh = lane >> 5, r = lane & 31, wu = threadIdx.x >> 6;
   const int NO = N / 2;
-  static_assert(Cfg::TNW % 2 == 0, "gate/up column-block pairs");
+  if constexpr (Cfg::TNW == 1) {
+    // one 32-column block per wave: gate blocks (even) and up blocks (odd) sit in neighbouring
+    // waves, so each gate wave parks silu(g) in LDS (rows padded to 33 floats) for its up wave
+    static_assert(Cfg::NW % 2 == 0, "gate/up wave pairs");
+    constexpr int RS = 33;
+    float* sg_lds = reinterpret_cast<float*>(smem) + (wu / 2) * Cfg::BM * RS;
+    if (wu % 2 == 0) {
 #pragma unroll
-  for (int jp = 0; jp < Cfg::TNW; jp += 2) {
-    const int ng = n0 + (wu * Cfg::TNW + jp) * 32;  // the pair's gate block; the up block follows
-    if (ng >= N) continue;
-    const int col = ng / 2 + r;
+      for (int i = 0; i < Cfg::TMW; ++i)
 #pragma unroll
-    for (int i = 0; i < Cfg::TMW; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = m0 + i * 32 + acc_row(e, hh);
-        if (m < M) {
-          const float g = acc[i][jp][e], u = acc[i][jp + 1][e];
-          const float sg = g / (1.0f + expf(-g));
-          C[(size_t)m * NO + col] = from_f32<bf16>(sg * u);
+        for (int e = 0; e < 16; ++e) {
+          const float g = acc[i][0][e];
+          sg_lds[(i * 32 + acc_row(e, hh)) * RS + r] = g / (1.0f + expf(-g));
         }
-      }
+    }
+    __syncthreads();
+    const int ng = n0 + (wu - 1) * 32;  // the pair's gate block
+    if (wu % 2 == 1 && ng < N) {
+      const int col = ng / 2 + r;
+#pragma unroll
+      for (int i = 0; i < Cfg::TMW; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = m0 + i * 32 + acc_row(e, hh);
+          if (m < M) C[(size_t)m * NO + col] = from_f32<bf16>(sg_lds[(i * 32 + acc_row(e, hh)) * RS + r] * acc[i][0][e]);
+        }
+    }
+  } else {
+    static_assert(Cfg::TNW % 2 == 0, "gate/up column-block pairs");
+#pragma unroll
+    for (int jp = 0; jp < Cfg::TNW; jp += 2) {
+      const int ng = n0 + (wu * Cfg::TNW + jp) * 32;  // the pair's gate block; the up block follows
+      if (ng >= N) continue;
+      const int col = ng / 2 + r;
+#pragma unroll
+      for (int i = 0; i < Cfg::TMW; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = m0 + i * 32 + acc_row(e, hh);
+          if (m < M) {
+            const float g = acc[i][jp][e], u = acc[i][jp + 1][e];
+            const float sg = g / (1.0f + expf(-g));
+            C[(size_t)m * NO + col] = from_f32<bf16>(sg * u);
+          }
+        }
+    }
   }
 }
 
@@ -480,8 +515,22 @@ __global__ void pack_gate_up_fragments_kernel(const bf16* __restrict__ g, const 
   *reinterpret_cast<bf16x8*>(p + packed_offset(n, k, N, K)) = *reinterpret_cast<const bf16x8*>(src);
 }
 
+// 2 * inter in whole 128x192 tiles (six waves) or else whole 128x256 tiles (four waves)
 bool rs_swiglu_ok(int inter, int hidden, int dtype) {
-  return dtype == ORTHRUS_BF16 && hidden == 64 * kRsStages && 2 * inter >= kWideN && (2 * inter) % RsSwiglu::BN == 0;
+  return dtype == ORTHRUS_BF16 && hidden == 64 * kRsStages && 2 * inter >= kWideN &&
+         ((2 * inter) % RsSwiglu192::BN == 0 || (2 * inter) % RsSwiglu::BN == 0);
+}
+
+template <typename Cfg>
+int32_t launch_rs_swiglu(int M, int N, int K, const void* a, const void* w, void* c, hipStream_t st) {
+  constexpr size_t epi = Cfg::TNW == 1 ? (size_t)(Cfg::NW / 2) * Cfg::BM * 33 * sizeof(float) : 0;
+  constexpr size_t lds = Cfg::RING > epi ? Cfg::RING : epi;
+  const int mtiles = (M + Cfg::BM - 1) / Cfg::BM, ntiles = N / Cfg::BN;
+  allow_lds(rs_swiglu_kernel<Cfg>, lds);
+  hipLaunchKernelGGL(rs_swiglu_kernel<Cfg>, dim3(mtiles * ntiles), dim3(Cfg::NT), lds, st,
+                     reinterpret_cast<const bf16*>(a), reinterpret_cast<const bf16*>(w), reinterpret_cast<bf16*>(c),
+                     M, N, K);
+  return check_launch("orthrus_gemm_swiglu_fragments");
 }
 
 template <typename T, typename OutT>
@@ -666,8 +715,9 @@ extern "C" int32_t orthrus_pack_gate_up_fragments(int32_t inter, int32_t hidden,
   ORTHRUS_REQUIRE(inter > 0 && hidden > 0 && gate && up && packed, ORTHRUS_ERR_INVALID_ARG,
                   "pack_gate_up_fragments: bad args");
   ORTHRUS_REQUIRE(rs_swiglu_ok(inter, hidden, dtype), ORTHRUS_ERR_UNSUPPORTED,
-                  "pack_gate_up_fragments: built for bf16, hidden %d and 2*inter a multiple of %d >= %d "
-                  "(got dtype %d, hidden %d, inter %d)", 64 * kRsStages, RsSwiglu::BN, kWideN, dtype, hidden, inter);
+                  "pack_gate_up_fragments: built for bf16, hidden %d and 2*inter a multiple of %d or %d, >= %d "
+                  "(got dtype %d, hidden %d, inter %d)", 64 * kRsStages, RsSwiglu192::BN, RsSwiglu::BN, kWideN, dtype,
+                  hidden, inter);
   ORTHRUS_REQUIRE(((reinterpret_cast<uintptr_t>(gate) | reinterpret_cast<uintptr_t>(up) |
                     reinterpret_cast<uintptr_t>(packed)) & 15) == 0, ORTHRUS_ERR_INVALID_ARG,
                   "pack_gate_up_fragments: pointers must be 16-byte aligned");
@@ -682,17 +732,14 @@ extern "C" int32_t orthrus_gemm_swiglu_fragments(int32_t M, int32_t inter, int32
                                                  const void* a, const void* w_fragments, void* c, void* stream) {
   ORTHRUS_REQUIRE(M >= 0 && inter > 0 && hidden > 0, ORTHRUS_ERR_INVALID_ARG, "gemm_swiglu_fragments: bad sizes");
   ORTHRUS_REQUIRE(rs_swiglu_ok(inter, hidden, dtype), ORTHRUS_ERR_UNSUPPORTED,
-                  "gemm_swiglu_fragments: built for bf16, hidden %d and 2*inter a multiple of %d >= %d",
-                  64 * kRsStages, RsSwiglu::BN, kWideN);
+                  "gemm_swiglu_fragments: built for bf16, hidden %d and 2*inter a multiple of %d or %d, >= %d",
+                  64 * kRsStages, RsSwiglu192::BN, RsSwiglu::BN, kWideN);
   ORTHRUS_REQUIRE(a && w_fragments && c, ORTHRUS_ERR_INVALID_ARG, "gemm_swiglu_fragments: null pointer");
   ORTHRUS_REQUIRE(((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(w_fragments)) & 15) == 0,
                   ORTHRUS_ERR_INVALID_ARG, "gemm_swiglu_fragments: a and w must be 16-byte aligned");
   if (M == 0) return ORTHRUS_OK;
   const int N = 2 * inter;
-  const int mtiles = (M + RsSwiglu::BM - 1) / RsSwiglu::BM, ntiles = N / RsSwiglu::BN;
-  allow_lds(rs_swiglu_kernel<RsSwiglu>, RsSwiglu::RING);
-  hipLaunchKernelGGL(rs_swiglu_kernel<RsSwiglu>, dim3(mtiles * ntiles), dim3(RsSwiglu::NT), RsSwiglu::RING,
-                     reinterpret_cast<hipStream_t>(stream), reinterpret_cast<const bf16*>(a),
-                     reinterpret_cast<const bf16*>(w_fragments), reinterpret_cast<bf16*>(c), M, N, hidden);
-  return check_launch("orthrus_gemm_swiglu_fragments");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (N % RsSwiglu192::BN == 0) return launch_rs_swiglu<RsSwiglu192>(M, N, hidden, a, w_fragments, c, st);
+  return launch_rs_swiglu<RsSwiglu>(M, N, hidden, a, w_fragments, c, st);
 }

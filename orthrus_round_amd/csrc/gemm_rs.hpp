@@ -41,28 +41,33 @@ struct RsCfg {
   static constexpr int TMW = TMW_, TNW = TNW_, NW = NW_, SA = SA_, NB = NB_;
   static constexpr int BM = 32 * TMW, BN = 32 * TNW * NW, NT = 64 * NW;
   static constexpr int A_STAGE = BM * 128;    // one stage of the activation tile in LDS
-  static constexpr int NLA = BM / (8 * NW);   // 1 KiB activation wave loads per wave per stage
+  // The activation stage is BM / 8 wave loads of 1 KiB, dealt round-robin to the waves: wave wu
+  // issues loads wu, wu + NW, ...; when NW does not divide them the first waves issue one more.
+  static constexpr int ALOADS = BM / 8;
+  static constexpr int NLA = (ALOADS + NW - 1) / NW;  // most activation loads of a wave per stage
+  static constexpr int NLA_MIN = ALOADS / NW;         // fewest
   static constexpr int NLW = TNW * 4;         // weight fragment loads per wave per stage
   static constexpr size_t RING = (size_t)SA * A_STAGE;
-  static_assert(NLA >= 1 && NLA * 8 * NW == BM, "activation rows split over the waves");
+  static_assert(NLA_MIN >= 1 && ALOADS * 8 == BM, "every wave issues activation loads");
   static_assert(NW % 2 == 0, "the activation swizzle assumes an even number of waves");
   static_assert(SA >= 2 && NB >= 1, "ring depths");
   // Loads issued after stage s's activation loads, when the stage count is NKS: the prologue
   // issues activation stages 0..SA-2 then weight stages 0..NB-1; stage t issues activation stage
   // t+SA-1 then weight stage t+NB, each only if it exists.  Waiting until at most that many loads
-  // are outstanding guarantees stage s's activations (loads complete in issue order).
+  // are outstanding guarantees stage s's activations (loads complete in issue order).  The count
+  // takes NLA_MIN activation loads per stage: a wave that issues more waits a little longer.
   static constexpr int vm_after_a(int s, int NKS) {
     auto a_exists = [&](int st) { return st < NKS; };
     auto w_exists = [&](int st) { return st < NKS; };
     int n = 0;
     if (s <= SA - 2) {
-      for (int st = s + 1; st <= SA - 2; ++st) n += a_exists(st) ? NLA : 0;
+      for (int st = s + 1; st <= SA - 2; ++st) n += a_exists(st) ? NLA_MIN : 0;
       for (int st = 0; st < NB; ++st) n += w_exists(st) ? NLW : 0;
-      for (int t = 0; t < s; ++t) n += (a_exists(t + SA - 1) ? NLA : 0) + (w_exists(t + NB) ? NLW : 0);
+      for (int t = 0; t < s; ++t) n += (a_exists(t + SA - 1) ? NLA_MIN : 0) + (w_exists(t + NB) ? NLW : 0);
     } else {
       const int t0 = s - SA + 1;  // the stage that issued stage s's activations
       n += w_exists(t0 + NB) ? NLW : 0;
-      for (int t = t0 + 1; t < s; ++t) n += (a_exists(t + SA - 1) ? NLA : 0) + (w_exists(t + NB) ? NLW : 0);
+      for (int t = t0 + 1; t < s; ++t) n += (a_exists(t + SA - 1) ? NLA_MIN : 0) + (w_exists(t + NB) ? NLW : 0);
     }
     return n < 63 ? n : 63;  // more than 63 outstanding cannot be expressed: wait a little longer
   }
@@ -94,10 +99,10 @@ __device__ __forceinline__ void rs_mainloop(const bf16* __restrict__ A, const bf
 #pragma unroll
     for (int j = 0; j < TNW; ++j) acc[i][j] = f32x16{};
 
-  // activation loads: load j of wave wu fills tile rows (NW*j + wu)*8 .. +7; lane l lands in row
-  // +l/8, 16-byte slot l%8, and fetches the chunk that slot holds under the swizzle (the swizzle
-  // of those rows is the same for every j since 4*NW*j is a multiple of 8).  Rows past M re-read
-  // row M-1; those outputs are never stored.
+  // activation loads: load j of wave wu fills tile rows (NW*j + wu)*8 .. +7 (when NW*j + wu <
+  // ALOADS); lane l lands in row +l/8, 16-byte slot l%8, and fetches the chunk that slot holds under
+  // the swizzle (the swizzle of those rows is the same for every j since 4*NW*j is a multiple of
+  // 8).  Rows past M re-read row M-1; those outputs are never stored.
   // addresses: a wave-uniform base plus a loop-invariant 32-bit per-lane byte offset
   uint32_t aoff[NLA];
 #pragma unroll
@@ -109,7 +114,9 @@ __device__ __forceinline__ void rs_mainloop(const bf16* __restrict__ A, const bf
     unsigned char* dst = lds + (s % SA) * Cfg::A_STAGE;
     const char* base = reinterpret_cast<const char*>(A + (size_t)(ks0 + s) * BK);
 #pragma unroll
-    for (int j = 0; j < NLA; ++j) load_to_lds16(base + aoff[j], dst + (NW * j + wu) * 8 * 128);
+    for (int j = 0; j < NLA; ++j)
+      if (NLA == Cfg::NLA_MIN || NW * j + wu < Cfg::ALOADS)  // wave-uniform
+        load_to_lds16(base + aoff[j], dst + (NW * j + wu) * 8 * 128);
   };
   // weight fragments of this wave's TNW column blocks: one 1 KiB contiguous wave load per
   // (block, k-step); blocks past N re-read the last block (their columns are never stored)

@@ -1,6 +1,8 @@
 // Host-side plumbing shared by all entry points: thread-local error string, status helpers,
 // ABI version.
 #include <cstdarg>
+#include <mutex>
+#include <vector>
 
 #include "common.hpp"
 
@@ -18,6 +20,16 @@ int32_t fail(int32_t status, const char* fmt, ...) {
   va_end(ap);
   g_last_error = buf;
   return status;
+}
+
+void allow_lds_once(const void* kernel, size_t bytes) {
+  static std::mutex mu;
+  static std::vector<const void*> done;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const void* k : done)
+    if (k == kernel) return;
+  (void)hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  done.push_back(kernel);
 }
 
 int32_t check_launch(const char* what) {

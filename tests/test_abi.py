@@ -71,6 +71,7 @@ def test_struct_layouts_match_header():
     (lambda: ora.pack_gate_up_fragments(8192, 4096, ora.BF16, 16, None, 16, stream=0), 1),
     (lambda: ora.pack_gate_up_fragments(8192, 4096, ora.BF16, 16, 24, 16, stream=0), 1),  # misaligned
     (lambda: ora.gemm_swiglu_fragments(8, 4096, 4096, ora.BF16, 16, 16, 16, stream=0), 2),  # 2I < 16384
+    (lambda: ora.gemm_swiglu_fragments(8, 8224, 4096, ora.BF16, 16, 16, 16, stream=0), 2),  # no whole tiles
     (lambda: ora.gemm_swiglu_fragments(8, 8192, 4096, ora.BF16, 16, None, 16, stream=0), 1),
     (lambda: ora.rejection_accept(2, 32, 1000, 0.8, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 8, 64, None,
                                   stream=0), 3),  # no workspace

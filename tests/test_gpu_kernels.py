@@ -349,12 +349,14 @@ def test_gemm_epilogues(dtype, M, N, K, epi):
     assert np.abs(out - ref).max() / np.abs(ref).max() <= tol
 
 
+@pytest.mark.parametrize("inter", [12288, 8192])
 @pytest.mark.parametrize("M", [256, 300, 65, 8])
-def test_gemm_swiglu_fragments_has_the_bits_of_the_row_packed_gemm(M):
-    """The register-streamed gate/up + SwiGLU on fragment-packed weights (hidden 4096, 2 x 8192
-    gate/up rows) gives exactly the bits of orthrus_gemm(SWIGLU) on the row-interleaved packing,
-    at whole and ragged 128-row tiles and at a few rows; both are also checked against float64."""
-    inter, H = 8192, 4096
+def test_gemm_swiglu_fragments_has_the_bits_of_the_row_packed_gemm(M, inter):
+    """The register-streamed gate/up + SwiGLU on fragment-packed weights (hidden 4096; 2 x 12288
+    gate/up rows take 128x192 tiles of six wavefronts, 2 x 8192 128x256 tiles of four) gives exactly
+    the bits of orthrus_gemm(SWIGLU) on the row-interleaved packing, at whole and ragged 128-row
+    tiles and at a few rows; both are also checked against float64."""
+    H = 4096
     a, w = synth.lmhead_inputs(22, max(M, 1), H, 2 * inter, h_std=1.0, w_std=0.02)
     a = a[:M]
     gate, up = dev(w[:inter], ora.BF16), dev(w[inter:], ora.BF16)
