@@ -266,7 +266,8 @@ def attention_c2(replays=50):
     """One attention layer at Qwen3-1.7B shape (batch 1, 16Q/8KV heads x 128, bf16 in, fp32 out,
     32 block queries, both masks) at cache lengths 1024, 4096 and 8192.  Each call is timed cold:
     the caches are evicted by a 512 MiB read before it.  These calls move 4.7 to 34 MB, below
-    launch scale (one workgroup per kv head and key chunk)."""
+    launch scale (one workgroup per kv head and key chunk), so shorter key chunks (more workgroups,
+    more partials for the combine) are timed beside the 1024- and 512-key ones."""
     import torch
     import orthrus_round_amd as ora
     import synth
@@ -280,7 +281,7 @@ def attention_c2(replays=50):
         q, pk, pv = dv(inp.q), dv(np.nan_to_num(inp.pages_k)), dv(np.nan_to_num(inp.pages_v))
         pt, cl, kb, vb = dv(inp.page_table, False), dv(inp.ctx, False), dv(inp.k_blk), dv(inp.v_blk)
         row = {}
-        for chunk in (0, 512):
+        for chunk in (0, 512, 256, 128):
             desc = ora.attn_desc(1, 16, 8, 128, 32, 16, maxp, maxp * 16, chunk, ora.BF16, ora.F32, 1.0)
             ws = torch.empty(max(16, ora.attn_workspace_bytes(desc)), dtype=torch.uint8, device="cuda")
             for name in ("draft", "verify"):
@@ -298,7 +299,7 @@ def attention_c2(replays=50):
         res[str(n)] = row
     return {"workload": "batch 1, 16Q/8KV x 128, 32 block queries, bf16 -> fp32, cold (caches evicted before "
                         "every call; warm_ms_stats: back-to-back calls, inputs cache-resident); kv_chunk 1024 (one "
-                        "chunk up to 1K keys) and 512 (more workgroups)", **res}
+                        "chunk up to 1K keys), 512, 256 and 128 (more workgroups, more partials to combine)", **res}
 
 
 def c1_tiny(n_tokens=256, reps=5):
