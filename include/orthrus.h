@@ -265,7 +265,8 @@ int32_t orthrus_pack_gate_up(int32_t inter, int32_t hidden, int32_t dtype, const
  * with a [M, H], fp32 accumulation in the one-loop k order, so c has exactly the bits of
  * orthrus_gemm(M, 2I, H, dtype, dtype, ORTHRUS_EPI_SWIGLU, a, w) on the row-interleaved packing.
  * Built for bf16 with H = 4096 and 2I >= 16384, a multiple of 192 (128x192 tiles of six
- * wavefronts) or else of 256 (128x256 tiles of four); other shapes return
+ * wavefronts, and two that load the activations) or else of 256 (128x256 tiles of four); other
+ * shapes return
  * ORTHRUS_ERR_UNSUPPORTED (use orthrus_gemm).  Pointers 16-byte aligned; no workspace. */
 int32_t orthrus_pack_gate_up_fragments(int32_t inter, int32_t hidden, int32_t dtype,
                                        const void* gate, const void* up, void* packed, void* stream);

@@ -435,11 +435,19 @@ int32_t launch_quarters(int M, int N, int K, int epi, const void* a, const void*
 constexpr int kRsStages = 64;  // K = 64 * 64 = 4096, the instantiated width
 using RsSwiglu = RsCfg<4, 2, 4, 2, 4>;
 // 128x192 tiles of six 128x32 wavefronts: 256 workgroups at M = 256 and N = 24576 (every CU busy,
-// against 192 with 128x256 tiles), 2.5 MiB of operands per workgroup instead of 3.
+// against 192 with 128x256 tiles), 2.5 MiB of operands per workgroup instead of 3.  Two more
+// wavefronts load the activation stages (a ring of four), so that the compute wavefronts' loads
+// are their weight stages alone (four in flight).
 #ifndef ORTHRUS_RS192_NB
-#define ORTHRUS_RS192_NB 6
+#define ORTHRUS_RS192_NB 4
 #endif
-using RsSwiglu192 = RsCfg<4, 1, 6, 2, ORTHRUS_RS192_NB>;
+#ifndef ORTHRUS_RS192_SA
+#define ORTHRUS_RS192_SA 4
+#endif
+#ifndef ORTHRUS_RS192_NL
+#define ORTHRUS_RS192_NL 2
+#endif
+using RsSwiglu192 = RsCfg<4, 1, 6, ORTHRUS_RS192_SA, ORTHRUS_RS192_NB, ORTHRUS_RS192_NL>;
 
 template <typename Cfg>
 __global__ __launch_bounds__(Cfg::NT) void rs_swiglu_kernel(const bf16* __restrict__ A, const bf16* __restrict__ Wp,
@@ -459,7 +467,7 @@ __global__ __launch_bounds__(Cfg::NT) void rs_swiglu_kernel(const bf16* __restri
     static_assert(Cfg::NW % 2 == 0, "gate/up wave pairs");
     constexpr int RS = 33;
     float* sg_lds = reinterpret_cast<float*>(smem) + (wu / 2) * Cfg::BM * RS;
-    if (wu % 2 == 0) {
+    if (wu % 2 == 0 && wu < Cfg::NW) {  // (waves past NW load activations only)
 #pragma unroll
       for (int i = 0; i < Cfg::TMW; ++i)
 #pragma unroll
@@ -470,7 +478,7 @@ __global__ __launch_bounds__(Cfg::NT) void rs_swiglu_kernel(const bf16* __restri
     }
     __syncthreads();
     const int ng = n0 + (wu - 1) * 32;  // the pair's gate block
-    if (wu % 2 == 1 && ng < N) {
+    if (wu % 2 == 1 && wu < Cfg::NW && ng < N) {
       const int col = ng / 2 + r;
 #pragma unroll
       for (int i = 0; i < Cfg::TMW; ++i)
@@ -482,6 +490,7 @@ __global__ __launch_bounds__(Cfg::NT) void rs_swiglu_kernel(const bf16* __restri
     }
   } else {
     static_assert(Cfg::TNW % 2 == 0, "gate/up column-block pairs");
+    if (wu >= Cfg::NW) return;  // a wave that loads activations only
 #pragma unroll
     for (int jp = 0; jp < Cfg::TNW; jp += 2) {
       const int ng = n0 + (wu * Cfg::TNW + jp) * 32;  // the pair's gate block; the up block follows

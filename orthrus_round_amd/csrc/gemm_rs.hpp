@@ -36,20 +36,26 @@ __host__ __device__ inline size_t packed_offset(int n, int k, int N, int K) {
   return ((((size_t)ks * nblk + nb) * 4 + kk) * 64 + (h * 32 + r)) * 8 + e;
 }
 
-template <int TMW_, int TNW_, int NW_, int SA_, int NB_>
+// NW compute wavefronts own the tile's column blocks.  With NL = 0 they also load the activation
+// stages; with NL > 0, NL more wavefronts do only that, so that a compute wave's vector-memory
+// counter tracks its weight loads alone and its wait for an activation stage (the barrier) never
+// drains weight loads still in flight.
+template <int TMW_, int TNW_, int NW_, int SA_, int NB_, int NL_ = 0>
 struct RsCfg {
-  static constexpr int TMW = TMW_, TNW = TNW_, NW = NW_, SA = SA_, NB = NB_;
-  static constexpr int BM = 32 * TMW, BN = 32 * TNW * NW, NT = 64 * NW;
+  static constexpr int TMW = TMW_, TNW = TNW_, NW = NW_, SA = SA_, NB = NB_, NL = NL_;
+  static constexpr int BM = 32 * TMW, BN = 32 * TNW * NW, NT = 64 * (NW + NL);
   static constexpr int A_STAGE = BM * 128;    // one stage of the activation tile in LDS
-  // The activation stage is BM / 8 wave loads of 1 KiB, dealt round-robin to the waves: wave wu
-  // issues loads wu, wu + NW, ...; when NW does not divide them the first waves issue one more.
+  // The activation stage is BM / 8 wave loads of 1 KiB, dealt round-robin to the AW loading waves:
+  // loading wave i issues loads i, i + AW, ...; when AW does not divide them the first waves issue
+  // one more.
+  static constexpr int AW = NL > 0 ? NL : NW;
   static constexpr int ALOADS = BM / 8;
-  static constexpr int NLA = (ALOADS + NW - 1) / NW;  // most activation loads of a wave per stage
-  static constexpr int NLA_MIN = ALOADS / NW;         // fewest
+  static constexpr int NLA = (ALOADS + AW - 1) / AW;  // most activation loads of a wave per stage
+  static constexpr int NLA_MIN = ALOADS / AW;         // fewest
   static constexpr int NLW = TNW * 4;         // weight fragment loads per wave per stage
   static constexpr size_t RING = (size_t)SA * A_STAGE;
   static_assert(NLA_MIN >= 1 && ALOADS * 8 == BM, "every wave issues activation loads");
-  static_assert(NW % 2 == 0, "the activation swizzle assumes an even number of waves");
+  static_assert(AW % 2 == 0, "the activation swizzle assumes an even number of loading waves");
   static_assert(SA >= 2 && NB >= 1, "ring depths");
   // Loads issued after stage s's activation loads, when the stage count is NKS: the prologue
   // issues activation stages 0..SA-2 then weight stages 0..NB-1; stage t issues activation stage
@@ -70,6 +76,13 @@ struct RsCfg {
       for (int t = t0 + 1; t < s; ++t) n += (a_exists(t + SA - 1) ? NLA_MIN : 0) + (w_exists(t + NB) ? NLW : 0);
     }
     return n < 63 ? n : 63;  // more than 63 outstanding cannot be expressed: wait a little longer
+  }
+  // The same for a loading wave of the NL > 0 layout, which issues activation loads only: stage
+  // s's have landed once those of stages s+1 .. s+SA-2 alone are outstanding.
+  static constexpr int vm_after_a_only(int s, int NKS) {
+    int n = 0;
+    for (int st = s + 1; st <= s + SA - 2; ++st) n += st < NKS ? NLA_MIN : 0;
+    return n < 63 ? n : 63;
   }
 };
 
@@ -92,31 +105,34 @@ __device__ __forceinline__ void rs_mainloop(const bf16* __restrict__ A, const bf
   using MF = Mfma<bf16>;
   constexpr int TMW = Cfg::TMW, TNW = Cfg::TNW, NW = Cfg::NW, SA = Cfg::SA, NB = Cfg::NB, NLA = Cfg::NLA;
   constexpr int BK = 64, EPC = 8;
+  constexpr int NL = Cfg::NL, AW = Cfg::AW;
   const int lane = threadIdx.x & 63, hh = lane >> 5, r = lane & 31;
   const int wu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool loader = NL > 0 && wu >= NW;  // a wave that only loads activations
+  const int ai = NL > 0 ? wu - NW : wu;     // this wave's index among the activation-loading waves
 #pragma unroll
   for (int i = 0; i < TMW; ++i)
 #pragma unroll
     for (int j = 0; j < TNW; ++j) acc[i][j] = f32x16{};
 
-  // activation loads: load j of wave wu fills tile rows (NW*j + wu)*8 .. +7 (when NW*j + wu <
-  // ALOADS); lane l lands in row +l/8, 16-byte slot l%8, and fetches the chunk that slot holds under
-  // the swizzle (the swizzle of those rows is the same for every j since 4*NW*j is a multiple of
-  // 8).  Rows past M re-read row M-1; those outputs are never stored.
+  // activation loads: load j of loading wave ai fills tile rows (AW*j + ai)*8 .. +7 (when AW*j + ai
+  // < ALOADS); lane l lands in row +l/8, 16-byte slot l%8, and fetches the chunk that slot holds
+  // under the swizzle (the swizzle of those rows is the same for every j since 4*AW*j is a multiple
+  // of 8).  Rows past M re-read row M-1; those outputs are never stored.
   // addresses: a wave-uniform base plus a loop-invariant 32-bit per-lane byte offset
   uint32_t aoff[NLA];
 #pragma unroll
   for (int j = 0; j < NLA; ++j) {
-    const int row = min(m0 + wu * 8 + (lane >> 3) + 8 * NW * j, M - 1);
-    aoff[j] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)(((lane & 7) ^ lds_swizzle(wu * 8 + (lane >> 3))) * 16);
+    const int row = min(m0 + ai * 8 + (lane >> 3) + 8 * AW * j, M - 1);
+    aoff[j] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)(((lane & 7) ^ lds_swizzle(ai * 8 + (lane >> 3))) * 16);
   }
   auto issue_a = [&](int s) __attribute__((always_inline)) {
     unsigned char* dst = lds + (s % SA) * Cfg::A_STAGE;
     const char* base = reinterpret_cast<const char*>(A + (size_t)(ks0 + s) * BK);
 #pragma unroll
     for (int j = 0; j < NLA; ++j)
-      if (NLA == Cfg::NLA_MIN || NW * j + wu < Cfg::ALOADS)  // wave-uniform
-        load_to_lds16(base + aoff[j], dst + (NW * j + wu) * 8 * 128);
+      if (NLA == Cfg::NLA_MIN || AW * j + ai < Cfg::ALOADS)  // wave-uniform
+        load_to_lds16(base + aoff[j], dst + (AW * j + ai) * 8 * 128);
   };
   // weight fragments of this wave's TNW column blocks: one 1 KiB contiguous wave load per
   // (block, k-step); blocks past N re-read the last block (their columns are never stored)
@@ -158,31 +174,47 @@ __device__ __forceinline__ void rs_mainloop(const bf16* __restrict__ A, const bf
     }
   };
 
-  WFrag wb[NB];
-  static_for<SA - 1>([&](auto sc) {
-    if constexpr (decltype(sc)::value < NKS) issue_a(decltype(sc)::value);
-  });
-  static_for<NB>([&](auto bc) {
-    if constexpr (decltype(bc)::value < NKS) issue_w(decltype(bc)::value, wb[decltype(bc)::value]);
-  });
   // The stage loop is unrolled completely (NKS is a compile-time count): a weight buffer loaded in
   // one stage and consumed NB stages later would be a loop-carried pending load, for which the
   // compiler's wait insertion falls back to draining every load at the loop head; in straight-line
   // code its wait before each stage's MFMAs counts exactly the loads issued after that buffer's.
-  static_for<NKS>([&](auto sc) {
-    constexpr int s = decltype(sc)::value;
-    constexpr int b = s % NB;
-    // stage s's activations have landed once only the loads issued after them are outstanding
-    waitcnt_vm<Cfg::vm_after_a(s, NKS)>();
-    // this wave's LDS reads of stage s-1 are complete before the barrier frees its slot
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0) only
-    __builtin_amdgcn_s_barrier();
-    if constexpr (s + SA - 1 < NKS) issue_a(s + SA - 1);  // into the slot of stage s-1, read by every wave
-    __builtin_amdgcn_sched_barrier(0);
-    compute(s, wb[b]);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (s + NB < NKS) issue_w(s + NB, wb[b]);
-  });
+  // Every wave executes the same NKS barriers, whichever role's loop it runs.
+  if (loader) {
+    static_for<SA - 1>([&](auto sc) {
+      if constexpr (decltype(sc)::value < NKS) issue_a(decltype(sc)::value);
+    });
+    static_for<NKS>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      waitcnt_vm<Cfg::vm_after_a_only(s, NKS)>();  // stage s's activations have landed
+      __builtin_amdgcn_s_barrier();
+      if constexpr (s + SA - 1 < NKS) issue_a(s + SA - 1);  // into the slot of stage s-1
+    });
+  } else {
+    WFrag wb[NB];
+    if constexpr (NL == 0) {
+      static_for<SA - 1>([&](auto sc) {
+        if constexpr (decltype(sc)::value < NKS) issue_a(decltype(sc)::value);
+      });
+    }
+    static_for<NB>([&](auto bc) {
+      if constexpr (decltype(bc)::value < NKS) issue_w(decltype(bc)::value, wb[decltype(bc)::value]);
+    });
+    static_for<NKS>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      constexpr int b = s % NB;
+      // stage s's activations have landed once only the loads issued after them are outstanding
+      // (with loading waves, their wait before the barrier covers it)
+      if constexpr (NL == 0) waitcnt_vm<Cfg::vm_after_a(s, NKS)>();
+      // this wave's LDS reads of stage s-1 are complete before the barrier frees its slot
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0) only
+      __builtin_amdgcn_s_barrier();
+      if constexpr (NL == 0 && s + SA - 1 < NKS) issue_a(s + SA - 1);  // into the slot of stage s-1
+      __builtin_amdgcn_sched_barrier(0);
+      compute(s, wb[b]);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (s + NB < NKS) issue_w(s + NB, wb[b]);
+    });
+  }
   // LDS is reused by the caller's epilogue
   __syncthreads();
 }
