@@ -350,7 +350,7 @@ def test_gemm_epilogues(dtype, M, N, K, epi):
 
 
 @pytest.mark.parametrize("inter", [12288, 8192])
-@pytest.mark.parametrize("M", [256, 300, 65, 8])
+@pytest.mark.parametrize("M", [256, 300, 65, 8, 1000])
 def test_gemm_swiglu_fragments_has_the_bits_of_the_row_packed_gemm(M, inter):
     """The register-streamed gate/up + SwiGLU on fragment-packed weights (hidden 4096; 2 x 12288
     gate/up rows take 128x192 tiles of six wavefronts, 2 x 8192 128x256 tiles of four) gives exactly
