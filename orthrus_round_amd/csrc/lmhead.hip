@@ -263,10 +263,13 @@ int32_t launch(LmArgs& a, bool sample, bool lse, hipStream_t st, int tile0 = 0, 
 template <typename T> using LmPairCfg = GemmCfg<T, 256, 256, 4, 2, 2, 2, true>;
 
 // Above 128 rows with an even number of k-stages: whole waves of 256x256 workgroups (eight 64x128
-// wavefronts, each owning one 128-column partial tile), then the remaining tiles as 256x128
-// workgroups in a second launch.  A 256x256 workgroup re-reads the 2 MiB activation tile from L2
-// once per 256 columns instead of once per 128, which is what bounds the LM head; a grid of only
-// 256x256 tiles would leave a last wave of 82 workgroups on 256 CUs at V = 151936, hence the mix.
+// wavefronts, each owning one 128-column partial tile), then the remaining tiles as 128x128
+// workgroups of four wavefronts in a second launch.  A 256x256 workgroup re-reads the 2 MiB
+// activation tile from L2 once per 256 columns instead of once per 128, which is what bounds the LM
+// head; a grid of only 256x256 tiles would leave a last wave of 82 workgroups on 256 CUs at
+// V = 151936, hence the mix.  The rest (163 tiles at M = 256) runs as 326 row-halves rather than
+// 163 workgroups of 256 rows, so more CUs share it (391-398 against 401-406 us per call); rows do
+// not change an element's k order, so the bits are the same.
 // The partials stay per 128-column tile, so the finalize merge is the same whatever the split.
 template <typename T>
 int32_t launch_mixed(LmArgs& a, bool sample, bool lse, hipStream_t st) {
@@ -280,7 +283,7 @@ int32_t launch_mixed(LmArgs& a, bool sample, bool lse, hipStream_t st) {
   const int rounds = (a.ntiles * mtiles) / (2 * cus);
   int npairs = std::min(a.ntiles / 2, rounds * cus / mtiles);
   if (int32_t s = launch<T, LmPairCfg<T>>(a, sample, lse, st, 0, npairs)) return s;
-  return launch<T, ORTHRUS_LM_HUGE_CFG(T)>(a, sample, lse, st, 2 * npairs);
+  return launch<T, ORTHRUS_LM_BIG_CFG(T)>(a, sample, lse, st, 2 * npairs);
 }
 
 }  // namespace
