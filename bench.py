@@ -39,7 +39,7 @@ def parse():
     p.add_argument("--counters", action="store_true",
                    help="hardware-counter mode: prefill, the timed rounds and the calibration copy only")
     p.add_argument("--block", type=int, default=32, help="rows per sequence of the timed rounds (block size K)")
-    p.add_argument("--match-tokens", type=int, default=64)
+    p.add_argument("--match-tokens", type=int, default=512)
     p.add_argument("--control-chunk", type=int, default=1024,
                    help="kv_chunk of the divergence control runs (another key summation order)")
     p.add_argument("--only", choices=["attn-c3"], default=None,
