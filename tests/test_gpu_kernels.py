@@ -74,8 +74,9 @@ def lse_f64(z, T=1.0):
 # ------------------------------------------------------------------- LM head
 
 # Above 128 rows: 511*128 + 77 columns are 512 tiles, two whole waves of 256x256 pair workgroups whose
-# last pair holds the ragged tile; 515 tiles at 300 rows leave a 256x128 rest of three tiles per row
-# tile; hidden 192 (an odd number of k-stages) takes the 256x128 layout alone.
+# last pair holds the ragged tile; 515 tiles at 300 rows leave a rest of three tiles, run as 128x128
+# row tiles (three of them, the last ragged); hidden 192 (an odd number of k-stages) takes the 256x128
+# layout alone.
 @pytest.mark.parametrize("rows,hidden,vocab,dtype", [(64, 256, 4096, ora.F32), (37, 256, 4000, ora.BF16),
                                                      (128, 512, 1024 + 64, ora.BF16), (8, 4096, 8192, ora.BF16),
                                                      (256, 256, 511 * 128 + 77, ora.BF16),
@@ -131,7 +132,8 @@ def test_lmhead_qwen3_8b_all_rows(c4):
 
 def test_lmhead_row_invariance(c4):
     """A row's token and logsumexp have the same bits whatever rows share the launch: 512 and 200
-    rows (256x256 pair tiles plus a 256x128 rest), 128, 64, 33, 7 and 1 (other tile shapes)."""
+    rows (256x256 pair tiles plus 128x128 row-halves of the rest), 128, 64, 33, 7 and 1 (other tile
+    shapes)."""
     h, w = c4
     full = lmhead(h, w, ora.BF16, block=1)
     for m in (200, 128, 64, 33, 7, 1):

@@ -34,7 +34,7 @@ def test_noalloc_lmhead_equals_workspace_call_twice():
     w_t = torch.from_numpy(w).to(torch.bfloat16).to(DEV)
     seqs = torch.arange(8, dtype=torch.int32, device=DEV)
     rnds = torch.full((8,), 2, dtype=torch.int32, device=DEV)
-    # first call: 256 rows, greedy (256x256 pair tiles plus a 256x128 rest)
+    # first call: 256 rows, greedy (256x256 pair tiles plus 128x128 row-halves of the rest)
     a = _call("ws", 256, hidden, vocab, h_t, w_t, 0.0, False, seqs, rnds, 32)
     b = _call("noalloc", 256, hidden, vocab, h_t, w_t, 0.0, False, seqs, rnds, 32)
     for x, y in zip(a, b):
