@@ -5,7 +5,8 @@
 // sec. 三: draft queries see the AR context before the block's anchor plus their whole block,
 // the AR path keeps the causal mask.
 //
-// Work decomposition (one workgroup = one (sequence, kv head, key chunk)):
+// Work decomposition (one workgroup = one (sequence, kv head, key chunk); the existing items take
+// the first slots of a grid sized for the longest context):
 //  * the G query heads that share a kv head are G wavefronts; each wavefront owns one query
 //    head's 32 block rows, so one K/V tile staged in LDS serves G*32 query rows (GQA reuse);
 //  * keys are streamed in 32-key tiles at absolute positions 32t..32t+31, gathered from the
@@ -41,7 +42,7 @@ struct AttnArgs {
   void* out;
   float* part_acc;
   float* part_ml;
-  int32_t Hq, Hkv, K, page, page_shift, max_pages, max_ctx, chunk, nchunk_max;
+  int32_t Hq, Hkv, K, page, page_shift, max_pages, max_ctx, chunk, nchunk_max, batch;
   float scale_log2;
 };
 
@@ -144,14 +145,47 @@ __global__ __launch_bounds__(64 * G) void attn_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   __shared__ int page_lds[kMaxChunkPages];
 
-  const int b = blockIdx.z, hk = blockIdx.y, c = blockIdx.x;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, hh = lane >> 5, r = lane & 31;
   const int K = a.K, C = a.chunk;
+  // The grid has nchunk_max x Hkv x batch slots, sized for the longest possible context.  The
+  // (sequence, kv head, chunk) items that exist take the first slots, in the order chunk fastest,
+  // then kv head, then sequence, and the remaining slots exit at once: a wave reads 64 sequences'
+  // lengths at a time, scans their item counts and finds the sequence that holds this slot.  Only
+  // the placement changes; each item is computed exactly as before.
+  const int id = blockIdx.x;
+  int seq = -1, first = 0, nch = 1;  // the slot's sequence, its first slot, its chunk count
+  for (int b0 = 0, base = 0; b0 < a.batch; b0 += 64) {
+    const int bi = b0 + lane;
+    int items = 0, nc = 1;
+    if (bi < a.batch) {
+      const int nl = a.ctx_len[bi];
+      nc = ((nl < 0) || (nl + K > a.max_ctx)) ? 1 : num_chunks<DRAFT>(nl, K, C);
+      items = nc * a.Hkv;
+    }
+    int incl = items;  // inclusive scan over the lanes
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
+    }
+    const int total = __shfl(incl, 63, 64);
+    if (id < base + total) {
+      const int L = __builtin_ctzll(__ballot(id < base + incl));
+      seq = b0 + L;
+      first = base + __shfl(incl, L, 64) - __shfl(items, L, 64);
+      nch = __shfl(nc, L, 64);
+      break;
+    }
+    base += total;
+  }
+  if (seq < 0) return;
+  const int b = __builtin_amdgcn_readfirstlane(seq);
+  const int nchunks = __builtin_amdgcn_readfirstlane(nch);
+  const int item = id - __builtin_amdgcn_readfirstlane(first);
+  const int hk = item / nchunks, c = item - hk * nchunks;
   const int n = a.ctx_len[b];
   const int hq = hk * G + w;
   const bool bad = (n < 0) || (n + K > a.max_ctx);
-  const int nchunks = bad ? 1 : num_chunks<DRAFT>(n, K, C);
-  if (c >= nchunks) return;
   OutT* out = reinterpret_cast<OutT*>(a.out);
   if (bad) {
     if (r < K) {
@@ -548,7 +582,7 @@ int32_t validate(const orthrus_attn_desc_t* d) {
 
 template <typename T, typename OutT, int D, int G, bool DRAFT>
 int32_t launch_t(const orthrus_attn_desc_t* d, AttnArgs& a, hipStream_t st) {
-  dim3 grid(a.nchunk_max, d->kv_heads, d->batch);
+  dim3 grid(a.nchunk_max * d->kv_heads * d->batch);  // slots past the existing items exit at once
   const size_t lds = AttnTile<T, D, G>::LDS_BYTES;
   allow_lds(attn_kernel<T, OutT, D, G, DRAFT>, lds);
   hipLaunchKernelGGL((attn_kernel<T, OutT, D, G, DRAFT>), grid, dim3(64 * G), lds, st, a);
@@ -588,7 +622,7 @@ int32_t run(const orthrus_attn_desc_t* d, const void* q, const void* kp, const v
   a.part_ml = a.nchunk_max > 1 ? a.part_acc + acc_elems : nullptr;
   a.Hq = d->q_heads; a.Hkv = d->kv_heads; a.K = d->block; a.page = d->page_size; a.max_pages = d->max_pages;
   a.page_shift = __builtin_ctz((unsigned)d->page_size);
-  a.max_ctx = d->max_ctx; a.chunk = chunk_of(d); a.scale_log2 = d->scale * kLog2e;
+  a.max_ctx = d->max_ctx; a.chunk = chunk_of(d); a.batch = d->batch; a.scale_log2 = d->scale * kLog2e;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (d->head_dim == 128) {
     if (G == 4) return dispatch_dtype<DRAFT, 128, 4>(d, a, st);
