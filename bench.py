@@ -31,7 +31,7 @@ def parse():
     p.add_argument("--layers", type=int, default=8)
     p.add_argument("--precision", default="bf16", choices=["bf16", "fp32"])
     p.add_argument("--kv-chunk", type=int, default=640)
-    p.add_argument("--attn-chunk", type=int, default=1536,
+    p.add_argument("--attn-chunk", type=int, default=1280,
                    help="kv_chunk of the batched attention measurement (16 ragged sequences up to 16K keys)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-attn", action="store_true")
