@@ -178,6 +178,23 @@ def test_verify_row_equals_one_row_ar_step(dtype):
         assert np.array_equal(one[0, 0], full[0, j]), j
 
 
+@pytest.mark.parametrize("draft", [True, False])
+def test_more_than_64_sequences(draft):
+    """70 ragged sequences (the grid's slots are matched to the existing chunks 64 sequences at a
+    time), several chunks each, one of them past the cache capacity: every sequence against the
+    oracle, the overflowing one all NaN."""
+    ctx = synth.ragged_lengths(11, 70, 0, 200)
+    ctx[66] = 230  # n + K = 262 > max_ctx = 256
+    inp = synth.attn_inputs(11, ctx, 8, 2, 128, block=32)
+    g = run_attn(inp, 8, 2, 128, 32, draft, kv_chunk=64, max_ctx=256)
+    assert np.isnan(g[66]).all()
+    for b in range(70):
+        if b == 66:
+            continue
+        o = oracle_attn(inp, b, 32, draft)
+        assert normwise(g[b], o) <= 2e-3, (b, int(ctx[b]))
+
+
 def test_capacity_overflow_marks_rows_nan():
     inp = synth.attn_inputs(7, np.array([40, 10]), 8, 2, 128, block=32)
     g = run_attn(inp, 8, 2, 128, 32, False, max_ctx=64)
