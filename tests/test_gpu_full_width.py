@@ -6,7 +6,8 @@ kernels and their launch configuration are those of the timed round (256-row GEM
 head, paged attention with the same kv_chunk).
 
 * Sequence 0's first round through the fp32 decoder (the same bf16-valued weights held in fp32)
-  against the oracle: the 32 draft ids and the 32 verify ids, where an id may differ only at an
+  against the oracle, after the 64-token prompts and after 700-token ones (two key chunks): the 32
+  draft ids and the 32 verify ids, where an id may differ only at an
   oracle near-tie (top two logits within 1e-4 relative); the verify pass is run by the oracle on
   the GPU's own drafts, since an ambiguous draft changes the verify inputs; then the accept count
   and the new KV length, which are integer logic on the GPU's own ids and must be exact.
@@ -45,9 +46,14 @@ def tie_ok(z, got, ref):
     return z[ref] - z[got] <= 1e-4 * max(1.0, abs(z[ref]))
 
 
-def test_first_round_matches_oracle(weights, prompts):
-    dec = Decoder(weights, SHAPE, precision="fp32", block=32, max_batch=8, max_ctx=P + 96, kv_chunk=KV_CHUNK)
-    dec.prefill(torch.from_numpy(prompts), max_out=64)
+@pytest.mark.parametrize("plen", [P, 700])
+def test_first_round_matches_oracle(weights, prompts, plen):
+    """plen 700 (two sequences): the cache spans two 640-key chunks, so the chunked attention and
+    its combine are on the checked path."""
+    pr = prompts if plen == P else synth.prompt_ids(SHAPE, 5, 2, plen)
+    dec = Decoder(weights, SHAPE, precision="fp32", block=32, max_batch=pr.shape[0], max_ctx=plen + 96,
+                  kv_chunk=KV_CHUNK)
+    dec.prefill(torch.from_numpy(pr), max_out=64)
     n0 = int(dec.ctx_len[0])
     dec.round_greedy()
     torch.cuda.synchronize()
@@ -58,8 +64,8 @@ def test_first_round_matches_oracle(weights, prompts):
     torch.cuda.empty_cache()
 
     Wt = M.Weights(weights, SHAPE)
-    cache, anchor = Dc.prefill(Wt, prompts[0], P + 96, rowwise=False)
-    assert cache.n == n0 == P - 1
+    cache, anchor = Dc.prefill(Wt, pr[0], plen + 96, rowwise=False)
+    assert cache.n == n0 == plen - 1
     zd = Dc.draft_pass(Wt, cache, [anchor] + [SHAPE.mask_id] * 31, rowwise=False)
     d_ref = M.argmax_lowest(zd)
     bad = [i for i in range(32) if not tie_ok(zd[i], d_gpu[i], d_ref[i])]
