@@ -1,9 +1,9 @@
 """GPU parity at the full-size round configuration: 8 decoder layers at Qwen3-8B width (hidden 4096,
 32Q/8KV heads x 128, SwiGLU 12288, vocabulary 151936), batch 8, the weights of the timed round.
 
-The prompts are 64 tokens so that the oracle (float64, BLAS over rows) finishes in seconds; the
-kernels and their launch configuration are those of the timed round (256-row GEMMs, 151936-wide LM
-head, paged attention with the same kv_chunk).
+The prompts are 64 tokens (700 in one case) so that the oracle (float64, BLAS over rows) finishes in
+seconds; the kernels and their launch configuration are those of the timed round (256-row GEMMs,
+151936-wide LM head, paged attention with the same kv_chunk).
 
 * Sequence 0's first round through the fp32 decoder (the same bf16-valued weights held in fp32)
   against the oracle, after the 64-token prompts and after 700-token ones (two key chunks): the 32
@@ -48,9 +48,9 @@ def tie_ok(z, got, ref):
 
 @pytest.mark.parametrize("plen", [P, 700])
 def test_first_round_matches_oracle(weights, prompts, plen):
-    """plen 700 (two sequences): the cache spans two 640-key chunks, so the chunked attention and
+    """plen 700: the cache spans two 640-key chunks, so the chunked attention and
     its combine are on the checked path."""
-    pr = prompts if plen == P else synth.prompt_ids(SHAPE, 5, 2, plen)
+    pr = prompts if plen == P else synth.prompt_ids(SHAPE, 5, 8, plen)
     dec = Decoder(weights, SHAPE, precision="fp32", block=32, max_batch=pr.shape[0], max_ctx=plen + 96,
                   kv_chunk=KV_CHUNK)
     dec.prefill(torch.from_numpy(pr), max_out=64)
